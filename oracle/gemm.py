@@ -1,0 +1,120 @@
+"""The two scaled-GEMM definitions in float64 -- oracle, test infrastructure.
+
+Mode (a), per-token x per-channel scales:
+    D[m,n] = sa[m] * sb[n] * sum_k dec(A[m,k]) * dec(B[n,k])
+A is [M,K] (tokens x hidden), B is [N,K] (output channels x hidden), both with
+K contiguous.  Source: the DeepGEMM call on the page
+"FP8 推理基础设施（五）：从 DeepGEMM 到 vLLM" (GEMM-call example: m = tokens,
+n, k = hidden, ``scale_a`` one fp32 per token, ``scale_b`` one fp32 per
+channel) and the shapes of its ``benchmark_gemm`` runs.
+
+The float64 sum is exact: every decoded value is an integer multiple of 2^-9
+below 2^9, so each product is a multiple of 2^-18 below 2^18, and any sum of
+fewer than 2^35 of them is a multiple of 2^-18 below 2^53.  Hence any
+summation order (a BLAS matmul included) gives the same float64 value.
+
+Mode (b), MXFP8 block scales (one UE8M0 code per 32 consecutive K elements of
+each row of A and of B; page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm 통합",
+sections 1 and 2):
+    D[m,n] = sum_j 2^(ea[m,j]-127) * 2^(eb[n,j]-127)
+                   * sum_{t<32} dec(A[m,32j+t]) * dec(B[n,32j+t])
+Each block sum is exact; the sum over blocks rounds in float64 only.
+
+Error bound for a GPU result accumulated in fp32 (stated for this library):
+    |D_gpu - D_ref| <= 1e-5 * W + ulp_out(D_ref)
+with W = |sa*sb| * sum_k |dec(A) dec(B)| (mode a) or the same sum with the
+block scale factors (mode b), and ulp_out the spacing of the output format
+at D_ref (bf16: 2^(max(floor(log2|x|),-126)-7), 2^-133 at zero; fp32: -23
+and 2^-149).
+"""
+
+import numpy as np
+
+from . import e4m3
+from .quant import MX_BLOCK, ue8m0_value
+
+REL_TOL = 1e-5
+
+
+def _decoded(codes):
+    d = e4m3.decode(codes)
+    if np.isnan(d).any():
+        raise ValueError("E4M3 NaN code in a GEMM operand")
+    return d
+
+
+def gemm_scaled(A, B, sa, sb) -> np.ndarray:
+    """Mode (a) result in float64 [M,N]."""
+    Ad, Bd = _decoded(A), _decoded(B)
+    S = Ad @ Bd.T                                   # exact (see module docstring)
+    sa = np.asarray(sa, dtype=np.float32).astype(np.float64)
+    sb = np.asarray(sb, dtype=np.float32).astype(np.float64)
+    return S * sa[:, None] * sb[None, :]
+
+
+def gemm_scaled_weight(A, B, sa, sb) -> np.ndarray:
+    """W[m,n] = |sa[m] sb[n]| * sum_k |dec(A[m,k]) dec(B[n,k])| (float64)."""
+    Ad, Bd = np.abs(_decoded(A)), np.abs(_decoded(B))
+    sa = np.abs(np.asarray(sa, dtype=np.float32).astype(np.float64))
+    sb = np.abs(np.asarray(sb, dtype=np.float32).astype(np.float64))
+    return (Ad @ Bd.T) * sa[:, None] * sb[None, :]
+
+
+def _mx_terms(A, B, ea, eb, absolute):
+    Ad, Bd = _decoded(A), _decoded(B)
+    if absolute:
+        Ad, Bd = np.abs(Ad), np.abs(Bd)
+    M, K = Ad.shape
+    N = Bd.shape[0]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32 for MX blocks")
+    nb = K // MX_BLOCK
+    ea = np.asarray(ea).reshape(M, nb)
+    eb = np.asarray(eb).reshape(N, nb)
+    D = np.zeros((M, N), dtype=np.float64)
+    for j in range(nb):
+        blk = slice(MX_BLOCK * j, MX_BLOCK * (j + 1))
+        Sj = Ad[:, blk] @ Bd[:, blk].T                       # exact block sum
+        D += ue8m0_value(ea[:, j])[:, None] * ue8m0_value(eb[:, j])[None, :] * Sj
+    return D
+
+
+def mxfp8_gemm(A, B, ea, eb) -> np.ndarray:
+    """Mode (b) result in float64 [M,N]."""
+    return _mx_terms(A, B, ea, eb, absolute=False)
+
+
+def mxfp8_gemm_weight(A, B, ea, eb) -> np.ndarray:
+    """Error-bound weight for mode (b): the same sum over |products|."""
+    return _mx_terms(A, B, ea, eb, absolute=True)
+
+
+def ulp(x, out_dtype: str) -> np.ndarray:
+    """Spacing of bf16 or fp32 at x (float64 array), subnormal floor included."""
+    mant_bits = {"bf16": 7, "f32": 23}[out_dtype]
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    # log2 of a float64 can misround just below a power of two; fix it exactly.
+    e = np.where(np.ldexp(1.0, e.astype(np.int64)) > x, e - 1, e)
+    e = np.where(np.ldexp(1.0, (e + 1).astype(np.int64)) <= x, e + 1, e)
+    e = np.maximum(e, -126)
+    return np.where(x > 0, np.ldexp(1.0, (e - mant_bits).astype(np.int64)),
+                    np.ldexp(1.0, -126 - mant_bits))
+
+
+def tolerance(D_ref, W, out_dtype: str) -> np.ndarray:
+    return REL_TOL * np.asarray(W, dtype=np.float64) + ulp(D_ref, out_dtype)
+
+
+def check(D_gpu, D_ref, W, out_dtype: str):
+    """Element-by-element comparison against the bound.
+
+    Returns (ok, worst error/tolerance ratio, number of elements over the bound).
+    """
+    D_gpu = np.asarray(D_gpu, dtype=np.float64)
+    err = np.abs(D_gpu - D_ref)
+    tol = tolerance(D_ref, W, out_dtype)
+    bad = ~(err <= tol)                 # NaN in D_gpu counts as a failure
+    ratio = float(np.max(np.where(np.isnan(err), np.inf, err / tol))) if err.size else 0.0
+    return (not bad.any()), ratio, int(bad.sum())

@@ -1,0 +1,200 @@
+"""Pins for the oracle's two GEMM definitions and its error bound (CPU only).
+
+  * exact rational brute force (fractions.Fraction, pure-Python loops) on tiny
+    shapes, for both modes;
+  * an integer cross-check: decoded values times 2^9 are integers, so the
+    mode-(a) sum times 2^18 must equal an int64 matmul bit for bit;
+  * closed forms: all-ones operands, one-hot (permutation) B, and the full
+    product table of every pair of finite codes against torch's decode;
+  * mode (b) special cases that reduce to mode (a), and the association of
+    each scale byte with its 32-element block;
+  * the bf16/fp32 ulp used by the bound, at known points.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import e4m3, gemm, quant
+
+
+def _codes(seed, shape):
+    return synth.u8_codes(seed, 1, shape)
+
+
+def _frac_dec(c):
+    return Fraction(e4m3.decode_code(int(c)))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (3, 2, 48), (3, 3, 33)])
+def test_mode_a_rational_brute_force(M, N, K):
+    A = _codes(100 + K, (M, K))
+    B = _codes(200 + K, (N, K))
+    sa = synth.scales(synth.WORKLOADS["c1_128x256x512"], "a")[:M]
+    sb = synth.scales(synth.WORKLOADS["c1_128x256x512"], "b")[:N]
+    D = gemm.gemm_scaled(A, B, sa, sb)
+    for m in range(M):
+        for n in range(N):
+            s = sum(_frac_dec(A[m, k]) * _frac_dec(B[n, k]) for k in range(K))
+            exact = s * Fraction(float(sa[m])) * Fraction(float(sb[n]))
+            # two float64 roundings after an exact sum
+            assert abs(Fraction(D[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (3, 2, 96)])
+def test_mode_b_rational_brute_force(M, N, K):
+    A = _codes(300 + K, (M, K))
+    B = _codes(400 + K, (N, K))
+    ea = synth.u8_codes(5, 2, (M, K // 32)) % 40 + 107
+    eb = synth.u8_codes(6, 3, (N, K // 32)) % 40 + 107
+    D = gemm.mxfp8_gemm(A, B, ea, eb)
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(0)
+            for k in range(K):
+                j = k // 32
+                scale = Fraction(2) ** (int(ea[m, j]) - 127) * Fraction(2) ** (int(eb[n, j]) - 127)
+                exact += scale * _frac_dec(A[m, k]) * _frac_dec(B[n, k])
+            assert abs(Fraction(D[m, n]) - exact) <= (K // 32) * Fraction(1, 2 ** 52) * \
+                sum(abs(_frac_dec(A[m, k]) * _frac_dec(B[n, k])) * Fraction(2) ** (int(ea[m, k // 32]) + int(eb[n, k // 32]) - 254)
+                    for k in range(K)) + Fraction(1, 2 ** 1000)
+
+
+def test_mode_a_integer_crosscheck():
+    M, N, K = 37, 29, 1000
+    A = _codes(11, (M, K))
+    B = _codes(12, (N, K))
+    # integer image of each code: dec * 2^9 (exact integers, from torch's decode)
+    ia = (torch.from_numpy(A).view(torch.float8_e4m3fn).to(torch.float64) * 512).to(torch.int64)
+    ib = (torch.from_numpy(B).view(torch.float8_e4m3fn).to(torch.float64) * 512).to(torch.int64)
+    S_int = (ia @ ib.T).numpy()
+    ones = np.ones(M, np.float32), np.ones(N, np.float32)
+    S = gemm.gemm_scaled(A, B, *ones)
+    assert np.array_equal(S * 2.0 ** 18, S_int.astype(np.float64))
+    assert np.all(np.abs(S_int) < 2 ** 53)
+
+
+def test_all_ones_closed_form():
+    M, N, K = 5, 7, 8192
+    A = np.full((M, K), 0x38, np.uint8)          # 1.0
+    B = np.full((N, K), 0x38, np.uint8)
+    sa = np.linspace(0.5, 2, M).astype(np.float32)
+    sb = np.linspace(2, 0.5, N).astype(np.float32)
+    D = gemm.gemm_scaled(A, B, sa, sb)
+    assert np.array_equal(D, 8192.0 * sa.astype(np.float64)[:, None] * sb.astype(np.float64)[None, :])
+
+
+def test_one_hot_b_picks_columns_of_a():
+    M, N, K = 6, 9, 64
+    A = _codes(21, (M, K))
+    perm = (np.arange(N) * 7 + 3) % K
+    B = np.zeros((N, K), np.uint8)
+    B[np.arange(N), perm] = 0x38
+    sa = np.arange(1, M + 1, dtype=np.float32)
+    sb = np.full(N, 0.5, np.float32)
+    D = gemm.gemm_scaled(A, B, sa, sb)
+    dec_a = torch.from_numpy(A).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = dec_a[:, perm] * sa[:, None] * 0.5
+    assert np.array_equal(D, want)
+
+
+def test_product_table_every_code_pair():
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    K = 64
+    A = np.zeros((finite.size, K), np.uint8)
+    B = np.zeros((finite.size, K), np.uint8)
+    A[:, 0] = finite
+    B[:, 0] = finite
+    D = gemm.gemm_scaled(A, B, np.ones(finite.size, np.float32), np.ones(finite.size, np.float32))
+    dec = torch.from_numpy(finite).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(D, np.outer(dec, dec))
+
+
+def test_mode_b_neutral_scales_equal_mode_a():
+    M, N, K = 8, 12, 256
+    A, B = _codes(31, (M, K)), _codes(32, (N, K))
+    ea = np.full((M, K // 32), 127, np.uint8)
+    eb = np.full((N, K // 32), 127, np.uint8)
+    ones_m, ones_n = np.ones(M, np.float32), np.ones(N, np.float32)
+    assert np.array_equal(gemm.mxfp8_gemm(A, B, ea, eb), gemm.gemm_scaled(A, B, ones_m, ones_n))
+
+
+def test_mode_b_row_constant_scales_equal_mode_a():
+    M, N, K = 8, 12, 256
+    A, B = _codes(33, (M, K)), _codes(34, (N, K))
+    alpha = (np.arange(M) * 5 % 23 + 115).astype(np.uint8)
+    beta = (np.arange(N) * 3 % 19 + 118).astype(np.uint8)
+    ea = np.repeat(alpha[:, None], K // 32, axis=1)
+    eb = np.repeat(beta[:, None], K // 32, axis=1)
+    sa = np.ldexp(1.0, alpha.astype(np.int64) - 127).astype(np.float32)
+    sb = np.ldexp(1.0, beta.astype(np.int64) - 127).astype(np.float32)
+    assert np.array_equal(gemm.mxfp8_gemm(A, B, ea, eb), gemm.gemm_scaled(A, B, sa, sb))
+
+
+def test_mode_b_scale_association():
+    """Only block j is nonzero, with one product: D = 2^(ea+eb-254) dec(a) dec(b)."""
+    K = 128
+    for j in range(K // 32):
+        for t in (0, 31):
+            A = np.zeros((3, K), np.uint8)
+            B = np.zeros((2, K), np.uint8)
+            A[:, 32 * j + t] = [0x38, 0x7E, 0x81]
+            B[:, 32 * j + t] = [0x40, 0xB9]
+            ea = np.full((3, 4), 127, np.uint8)
+            eb = np.full((2, 4), 127, np.uint8)
+            ea[:, j] = [100, 150, 127]
+            eb[:, j] = [130, 90]
+            D = gemm.mxfp8_gemm(A, B, ea, eb)
+            da = np.array([1.0, 448.0, -2.0 ** -9])
+            db = np.array([2.0, -1.125])
+            sa = np.ldexp(1.0, np.array([100, 150, 127]) - 127)
+            sb = np.ldexp(1.0, np.array([130, 90]) - 127)
+            assert np.array_equal(D, np.outer(da * sa, db * sb))
+
+
+def test_mx_quantized_gemm_tracks_fp32_product():
+    """Quantize fp32 operands with the MX rule; the MX GEMM stays near the
+    float64 product of the unquantized inputs (sanity, not a tight pin)."""
+    w = synth.WORKLOADS["c5_mx_4096x14336x4096"]
+    xa = synth.draw(w, "a", slice(0, 8))[:, :512]
+    xb = synth.draw(w, "b", slice(0, 8))[:, :512]
+    qa, ea = quant.mx_quantize(xa)
+    qb, eb = quant.mx_quantize(xb)
+    D = gemm.mxfp8_gemm(qa, qb, ea, eb)
+    ref = xa.astype(np.float64) @ xb.astype(np.float64).T
+    W = np.abs(xa).astype(np.float64) @ np.abs(xb).astype(np.float64).T
+    assert np.all(np.abs(D - ref) <= 0.13 * W)
+
+
+def test_ulp_values():
+    x = np.array([1.0, 1.5, 2.0 ** -130, 0.0, -3.0, 2.0 ** 20 - 1, 2.0 ** -126])
+    assert list(gemm.ulp(x, "bf16")) == [2.0 ** -7, 2.0 ** -7, 2.0 ** -133, 2.0 ** -133,
+                                         2.0 ** -6, 2.0 ** 12, 2.0 ** -133]
+    assert list(gemm.ulp(x, "f32")) == [2.0 ** -23, 2.0 ** -23, 2.0 ** -149, 2.0 ** -149,
+                                        2.0 ** -22, 2.0 ** -4, 2.0 ** -149]
+    # just below a power of two (log2 can round up there)
+    y = np.nextafter(np.ldexp(1.0, np.arange(-100, 100)), 0)
+    assert np.array_equal(gemm.ulp(y, "bf16"), np.ldexp(1.0, np.arange(-101, 99) - 7).clip(2.0 ** -133))
+
+
+def test_check_accepts_bf16_rounding_and_rejects_errors():
+    M, N, K = 16, 16, 512
+    A, B = _codes(41, (M, K)), _codes(42, (N, K))
+    sa = np.ones(M, np.float32)
+    sb = np.ones(N, np.float32)
+    D = gemm.gemm_scaled(A, B, sa, sb)
+    W = gemm.gemm_scaled_weight(A, B, sa, sb)
+    bf16 = torch.from_numpy(D).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    ok, ratio, nbad = gemm.check(bf16, D, W, "bf16")
+    assert ok and nbad == 0
+    wrong = bf16.copy()
+    wrong[3, 4] = -wrong[3, 4] + 1.0
+    assert not gemm.check(wrong, D, W, "bf16")[0]
+    transposed = gemm.gemm_scaled(A, B, sa, sb).T.copy()
+    assert not gemm.check(transposed, D, W, "bf16")[0]
+    nan = bf16.copy()
+    nan[0, 0] = np.nan
+    assert not gemm.check(nan, D, W, "bf16")[0]
