@@ -1,0 +1,211 @@
+"""Benchmark of the FP8 scaled-GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM:
+  ffn_up (default, 8192 x 22016 x 8192, per-token / per-channel scales):
+      fp8_quantize_rowwise(X_A) -> A, sa      (activations, per token)
+      fp8_quantize_rowwise(X_B) -> B, sb      (weights, per output channel)
+      fp8_gemm_scaled(A, B, sa, sb) -> D      (bf16)
+  mx (4096 x 14336 x 4096, MXFP8): mxfp8_gemm on E4M3 codes + UE8M0 scales
+      produced by the MX quantizer kernel from the fp32 operands.
+`value` = 2 M N K / (mean step time), in TFLOP/s.  Prints one JSON line.
+
+The line also carries
+  roofline:     the GEMM kernel alone (the dominant kernel): algorithmic flops
+                per launch / its mean duration from HIP events recorded on the
+                launch stream over the timed region, against the dense FP8 MFMA
+                peak of MI355X (5.0 PFLOP/s);
+  cpu_baseline: the CPU oracle (numpy, float64) timed on this host on a bounded
+                sample of the same workload, in the same unit.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"ffn_up": "c4_ffn_up_8192x22016x8192", "mx": "c5_mx_4096x14336x4096"}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic", default=None,
+                   help="JSON file with measured HBM bytes per GEMM launch (from rocprofv3 counters)")
+    return p.parse_args()
+
+
+def cpu_baseline_ffn_up(w, m_s=512, n_s=4096):
+    """The oracle on a sample: rows 0..m_s of the activations, rows 0..n_s of the
+    weights: quantize both (row-wise) and form the m_s x n_s block of D."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import gemm, quant
+    XA = synth.draw(w, "a", slice(0, m_s))
+    XB = synth.draw(w, "b", slice(0, n_s))
+    t0 = time.perf_counter()
+    qa = np.empty(XA.shape, np.uint8)
+    qb = np.empty(XB.shape, np.uint8)
+    sa = np.empty(m_s, np.float32)
+    sb = np.empty(n_s, np.float32)
+    for r in range(0, m_s, 256):
+        qa[r:r + 256], sa[r:r + 256] = quant.quantize_rowwise(XA[r:r + 256])
+    for r in range(0, n_s, 256):
+        qb[r:r + 256], sb[r:r + 256] = quant.quantize_rowwise(XB[r:r + 256])
+    gemm.gemm_scaled(qa, qb, sa, sb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * m_s * n_s * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "oracle row-wise quantize of activation rows 0..%d and weight rows 0..%d, then the "
+                      "%dx%dx%d block of D in float64 (numpy matmul); value = 2*%d*%d*%d flops / time"
+                      % (m_s, n_s, m_s, n_s, w.K, m_s, n_s, w.K)}
+
+
+def cpu_baseline_mx(w, m_s=512, n_s=2048):
+    from oracle import gemm, quant
+    XA = synth.draw(w, "a", slice(0, m_s))
+    XB = synth.draw(w, "b", slice(0, n_s))
+    t0 = time.perf_counter()
+    qa, ea = quant.mx_quantize(XA)
+    qb, eb = quant.mx_quantize(XB)
+    gemm.mxfp8_gemm(qa, qb, ea, eb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * m_s * n_s * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "oracle MX quantize of rows 0..%d / 0..%d, then the %dx%dx%d block of D in float64"
+                      % (m_s, n_s, m_s, n_s, w.K)}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_scaled_gemm_amd as fp8g
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fp8g.load()
+    w = synth.WORKLOADS[WORKLOADS[args.workload]]
+    dev = torch.device("cuda", 0)
+
+    log("drawing", w.name)
+    XA = torch.from_numpy(synth.draw(w, "a")).to(dev)
+    XB = torch.from_numpy(synth.draw(w, "b")).to(dev)
+    M, N, K = w.M, w.N, w.K
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    if w.mode == "a":
+        qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        qb = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+        sb = torch.empty((N,), dtype=torch.float32, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fp8g.fp8_quantize_rowwise(XA, qa, sa)
+            if ev is not None:
+                ev[1].record(stream)
+            fp8g.fp8_quantize_rowwise(XB, qb, sb)
+            if ev is not None:
+                ev[2].record(stream)
+            fp8g.fp8_gemm_scaled(M, N, K, qa, qb, sa, sb, D=D)
+            if ev is not None:
+                ev[3].record(stream)
+        kernels = ["quantize_activations", "quantize_weights", "gemm"]
+    else:
+        raise SystemExit("mx workload needs the GPU MX quantizer")
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+                  for j, k in enumerate(kernels)}      # microseconds
+
+    ms_per_step = elapsed / args.steps * 1e3
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_us = per_kernel["gemm"]
+    achieved = flops / (gemm_us * 1e-6) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("gemm_bytes_per_launch")
+    line = {
+        "metric": "FP8 GEMM TFLOP/s and % of FP8 MFMA peak at MxNxK=8192x22016x8192"
+                  if args.workload == "ffn_up" else "MXFP8 GEMM TFLOP/s at 4096x14336x4096",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "N": N, "K": K, "out": "bf16",
+                   "mode": "per-token x per-channel scales" if w.mode == "a" else "MXFP8",
+                   "step": " -> ".join(kernels)},
+        "pct_of_fp8_peak_step": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_fp8_kernel", "flops_per_launch": flops},
+    }
+    if w.mode == "a":
+        qbytes = {"quantize_activations": M * K * 5 + 4 * M, "quantize_weights": N * K * 5 + 4 * N}
+        line["quantizer_gbs"] = {k: round(b / (per_kernel[k] * 1e-6) / 1e9, 1) for k, b in qbytes.items()}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline_ffn_up(w) if w.mode == "a" else cpu_baseline_mx(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

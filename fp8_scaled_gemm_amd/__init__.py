@@ -1,0 +1,191 @@
+"""fp8g -- FP8 (E4M3) scaled GEMM and row-wise quantizer for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/fp8g.h`` (libfp8g.so, built
+in-tree by ``python -m fp8_scaled_gemm_amd.build``).  Every computation runs in
+the library's HIP kernels; this module only checks tensors, allocates outputs
+with torch, and passes raw device pointers and torch's current HIP stream.
+There is no fallback: if the library is missing, every call raises.
+
+Functions keep the C names and argument order:
+
+    fp8_quantize_rowwise(x)                              -> (q, scale)
+    fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
+    mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
+
+E4M3 tensors are ``torch.float8_e4m3fn`` (OCP, the gfx950 format) or raw
+``torch.uint8`` codes; the FNUZ variant of gfx942 is rejected.
+"""
+
+import ctypes
+import os
+import re
+
+__all__ = ["load", "fp8_quantize_rowwise", "fp8_gemm_scaled", "mxfp8_gemm", "status_string",
+           "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8g.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8g.h")
+OUT_BF16, OUT_F32 = 0, 1
+
+_lib = None
+
+_VOIDP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "fp8_quantize_rowwise": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
+    "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
+    "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
+}
+
+
+class Fp8gError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: status %d (%s)" % (where, status, status_string(status)))
+
+
+def header_functions():
+    """Names of the functions declared in include/fp8g.h."""
+    text = open(HEADER_PATH).read()
+    return re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def load():
+    """Load libfp8g.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfp8g.so is not built; run `python -m fp8_scaled_gemm_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.fp8g_status_string.argtypes = [ctypes.c_int]
+        lib.fp8g_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().fp8g_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise Fp8gError(status, where)
+
+
+# ----------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _as_codes(t, name):
+    torch = _torch()
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == getattr(torch, "float8_e4m3fnuz", None):
+        raise TypeError("%s: float8_e4m3fnuz (gfx942) is not the OCP E4M3FN format used on gfx950" % name)
+    raise TypeError("%s must be float8_e4m3fn or uint8 codes, got %s" % (name, t.dtype))
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _out_code(out_dtype):
+    torch = _torch()
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    if out_dtype == torch.float32:
+        return OUT_F32
+    raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def fp8_quantize_rowwise(x, q=None, scale=None):
+    """Per-row E4M3 quantization of a 2-D fp32 device tensor.
+
+    Returns (q: float8_e4m3fn [R, C], scale: float32 [R]) with x ~ q * scale.
+    ``q`` and ``scale`` may be passed in (uint8 or float8_e4m3fn / float32).
+    """
+    torch = _torch()
+    _need(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty((R,), dtype=torch.float32, device=x.device)
+    qc = _as_codes(q, "q")
+    _need(qc, "q", shape=(R, C))
+    _need(scale, "scale", torch.float32, (R,))
+    _check(load().fp8_quantize_rowwise(_ptr(x), R, C, _ptr(qc), _ptr(scale), _stream()),
+           "fp8_quantize_rowwise")
+    return q, scale
+
+
+def _gemm_operands(m, n, k, A, B):
+    Ac, Bc = _as_codes(A, "A"), _as_codes(B, "B")
+    _need(Ac, "A", shape=(m, k))
+    _need(Bc, "B", shape=(n, k))
+    return Ac, Bc
+
+
+def _out(m, n, A, D, out_dtype):
+    torch = _torch()
+    code = _out_code(out_dtype)
+    if D is None:
+        D = torch.empty((m, n), dtype=out_dtype, device=A.device)
+    _need(D, "D", out_dtype, (m, n))
+    return D, code
+
+
+def fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
+    """D[m,n] = scale_a[m] * scale_b[n] * sum_k A[m,k] * B[n,k] (A [m,k], B [n,k])."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    Ac, Bc = _gemm_operands(m, n, k, A, B)
+    _need(scale_a, "scale_a", torch.float32, (m,))
+    _need(scale_b, "scale_b", torch.float32, (n,))
+    D, code = _out(m, n, A, D, out_dtype)
+    _check(load().fp8_gemm_scaled(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D),
+                                  code, _stream()), "fp8_gemm_scaled")
+    return D
+
+
+def mxfp8_gemm(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
+    """MXFP8 GEMM: scale_a [m, k/32] and scale_b [n, k/32] are UE8M0 codes (uint8)."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    Ac, Bc = _gemm_operands(m, n, k, A, B)
+    if k % 32:
+        raise ValueError("k must be a multiple of 32 for MXFP8")
+    _need(scale_a, "scale_a", torch.uint8, (m, k // 32))
+    _need(scale_b, "scale_b", torch.uint8, (n, k // 32))
+    D, code = _out(m, n, A, D, out_dtype)
+    _check(load().mxfp8_gemm(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D), code,
+                             _stream()), "mxfp8_gemm")
+    return D

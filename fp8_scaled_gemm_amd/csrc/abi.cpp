@@ -1,0 +1,109 @@
+// C ABI of fp8g: host-side argument checks, then one kernel launch on the
+// caller's stream.  Every check runs before any HIP call, so a rejected call
+// queues nothing and touches no device.
+
+#include "fp8g.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// a * b * c, or -1 on overflow past 2^62
+int64_t mul3(int64_t a, int64_t b, int64_t c) {
+    const int64_t lim = (int64_t)1 << 62;
+    if (a == 0 || b == 0 || c == 0) return 0;
+    if (a > lim / b) return -1;
+    const int64_t ab = a * b;
+    if (ab > lim / c) return -1;
+    return ab * c;
+}
+
+int check_gemm_common(int64_t m, int64_t n, int64_t k, const void* A, const void* B, const void* sa,
+                      const void* sb, int64_t sa_bytes, int64_t sb_bytes, const void* D, int out_dtype) {
+    if (m < 0 || n < 0 || k < 0) return FP8G_ERR_SHAPE;
+    if (out_dtype != FP8G_OUT_BF16 && out_dtype != FP8G_OUT_F32) return FP8G_ERR_DTYPE;
+    if (m == 0 || n == 0) return FP8G_OK;  // nothing to write
+    const int64_t esz = out_dtype == FP8G_OUT_F32 ? 4 : 2;
+    const int64_t a_bytes = mul3(m, k, 1), b_bytes = mul3(n, k, 1), d_bytes = mul3(m, n, esz);
+    if (a_bytes < 0 || b_bytes < 0 || d_bytes < 0) return FP8G_ERR_UNSUPPORTED;
+    if (!D) return FP8G_ERR_NULL;
+    if (k > 0 && (!A || !B)) return FP8G_ERR_NULL;
+    if (sa_bytes > 0 && !sa) return FP8G_ERR_NULL;
+    if (sb_bytes > 0 && !sb) return FP8G_ERR_NULL;
+    if (!aligned16(D) || (A && !aligned16(A)) || (B && !aligned16(B)) || (sa && !aligned16(sa)) ||
+        (sb && !aligned16(sb)))
+        return FP8G_ERR_ALIGN;
+    const Range d = range_of(D, d_bytes);
+    if (overlaps(d, range_of(A, a_bytes)) || overlaps(d, range_of(B, b_bytes)) ||
+        overlaps(d, range_of(sa, sa_bytes)) || overlaps(d, range_of(sb, sb_bytes)))
+        return FP8G_ERR_OVERLAP;
+    return -1;  // go on
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8G_OK : FP8G_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                         hipStream_t stream) {
+    if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+    if (rows == 0) return FP8G_OK;
+    const int64_t n = mul3(rows, cols, 1);
+    if (n < 0 || n > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (!scale) return FP8G_ERR_NULL;
+    if (n > 0 && (!x || !q)) return FP8G_ERR_NULL;
+    if (!aligned16(scale) || (x && !aligned16(x)) || (q && !aligned16(q))) return FP8G_ERR_ALIGN;
+    const Range rx = range_of(x, n * 4), rq = range_of(q, n), rs = range_of(scale, rows * 4);
+    if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return FP8G_ERR_OVERLAP;
+    return hip_status(fp8g::launch_quantize_rowwise(x, rows, cols, q, scale, stream));
+}
+
+int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* scale_a,
+                    const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * 4, n * 4, D, out_dtype);
+    if (st >= 0) return st;
+    if (k % 16 != 0) return FP8G_ERR_UNSUPPORTED;
+    return hip_status(fp8g::launch_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D,
+                                               out_dtype == FP8G_OUT_F32, stream));
+}
+
+int mxfp8_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const uint8_t* scale_a,
+               const uint8_t* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    if (m >= 0 && n >= 0 && k >= 0 && k % 32 != 0) return FP8G_ERR_SHAPE;
+    const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * (k / 32), n * (k / 32), D, out_dtype);
+    if (st >= 0) return st;
+    return hip_status(fp8g::launch_gemm_mx(m, n, k, A, B, scale_a, scale_b, D, out_dtype == FP8G_OUT_F32, stream));
+}
+
+const char* fp8g_status_string(int status) {
+    switch (status) {
+        case FP8G_OK: return "ok";
+        case FP8G_ERR_NULL: return "a required pointer is NULL";
+        case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k not a multiple of 32 for MXFP8)";
+        case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case FP8G_ERR_DTYPE: return "unknown output dtype";
+        case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
+        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (k % 16 for fp8_gemm_scaled, or size overflow)";
+        case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

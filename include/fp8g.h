@@ -1,0 +1,141 @@
+/*
+ * fp8g -- FP8 (OCP E4M3FN) scaled GEMM and row-wise quantizer for AMD Instinct
+ * MI355X (gfx950).  Plain C ABI: host-side sizes, device pointers, a HIP
+ * stream.  No library state, no allocation, no synchronization.
+ *
+ * Operations (definitions in each entry point's comment):
+ *   fp8_quantize_rowwise  fp32 [rows, cols] -> E4M3 codes + one fp32 scale per row
+ *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
+ *   mxfp8_gemm            same product with one power-of-two scale per 32 K
+ *                         elements of every row of A and of B (MXFP8)
+ *
+ * Common conventions
+ *   - Every array is dense and row-major; the caller owns all memory.  A is
+ *     [m, k] and B is [n, k], both with k contiguous ("K-major"); D is
+ *     [m, n] with n contiguous.  E4M3 operands are passed as their byte codes.
+ *   - Device pointers must stay valid until the work queued on `stream`
+ *     has run.  `stream` may be 0 (the null stream).
+ *   - Every pointer must be 16-byte aligned (else FP8G_ERR_ALIGN), except
+ *     that an argument whose array is empty may be NULL.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns its status and queues nothing.  A launch failure returns
+ *     FP8G_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronization, as with any HIP kernel.
+ *   - Results are bitwise reproducible run to run (no atomics, fixed order).
+ *   - Calls are thread-safe: the library keeps no mutable state.
+ */
+#ifndef FP8G_H
+#define FP8G_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8G_OUT_BF16 = 0, /* bfloat16, round to nearest even */
+    FP8G_OUT_F32 = 1   /* float32 */
+} fp8g_out_t;
+
+typedef enum {
+    FP8G_OK = 0,
+    FP8G_ERR_NULL = 1,        /* required pointer is NULL */
+    FP8G_ERR_SHAPE = 2,       /* negative extent, or k not a multiple of 32 for MXFP8 */
+    FP8G_ERR_ALIGN = 3,       /* pointer not 16-byte aligned */
+    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype */
+    FP8G_ERR_OVERLAP = 5,     /* an output overlaps an input or another output */
+    FP8G_ERR_UNSUPPORTED = 6, /* valid but outside this build's limits (see each call) */
+    FP8G_ERR_HIP = 7          /* the HIP runtime refused the launch */
+} fp8g_status_t;
+
+/*
+ * fp8_quantize_rowwise -- per-row (per-token / per-channel) E4M3 quantization.
+ *
+ * Source: the scale rule abs_max / 448 (448 = largest E4M3 magnitude) in
+ * `_calibrate_scales` of the hybrid-inference class on the page
+ * "FP8 推理基础设施（五）：从 DeepGEMM 到 vLLM", applied per row as the
+ * per-token scale_a / per-channel scale_b of the same page's DeepGEMM call;
+ * the activation flow of section 2.2 of the RTX 4060 FP8 inference page.
+ *
+ *   s[r]   = fp32(max_c |x[r,c]| / 448)                  (IEEE division)
+ *   q[r,c] = E4M3_RNE_SAT(fp32(x[r,c] / s[r]))           (IEEE division, then
+ *            round to nearest even with ties to the even code, magnitudes
+ *            above 448 saturate to 448, sign copied from x)
+ *   if s[r] == 0 (zero or empty row, or amax/448 underflows): s[r] = 0 and
+ *   q[r,c] is +0 or -0 by the sign of x[r,c].
+ * The scale is a dequantization multiplier: x ~ decode(q) * s.
+ *
+ * x      device, fp32 [rows, cols], read only
+ * q      device, E4M3 codes [rows, cols], written
+ * scale  device, fp32 [rows], written
+ * rows, cols >= 0; rows == 0 is a no-op; cols == 0 writes scale = 0.
+ * NaN/Inf in x are outside the contract.  Bit-exact with the definition.
+ * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_ALIGN, ERR_OVERLAP, ERR_HIP.
+ */
+int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
+                         uint8_t* q, float* scale, hipStream_t stream);
+
+/*
+ * fp8_gemm_scaled -- FP8 GEMM with per-token A scales and per-channel B scales.
+ *
+ * Source: the DeepGEMM call on the page "FP8 推理基础设施（五）：从 DeepGEMM
+ * 到 vLLM" (GEMM-call example): E4M3 A and B, m = tokens, n, k = hidden,
+ * scale_a one fp32 per token, scale_b one fp32 per channel; argument order
+ * m, n, k, A, B, scale_a, scale_b as there.
+ *
+ *   D[m,n] = out( sa[m] * sb[n] * sum_k dec(A[m,k]) * dec(B[n,k]) )
+ * with the sum accumulated in fp32 on the matrix cores, the two scales
+ * applied in fp32, and `out` the conversion to bf16 (round to nearest even)
+ * or fp32.  Accuracy: |D - exact| <= 1e-5 * |sa sb| sum_k |dec(A) dec(B)|
+ * + 1 ulp of the output format.
+ *
+ * A        device, E4M3 codes [m, k]          B   device, E4M3 codes [n, k]
+ * scale_a  device, fp32 [m]                   scale_b device, fp32 [n]
+ * D        device, [m, n] of out_dtype (fp8g_out_t), written
+ * m, n, k >= 0.  m == 0 or n == 0: no-op.  k == 0: D = 0.
+ * Limits: k % 16 != 0 -> ERR_UNSUPPORTED (16-byte rows).  E4M3 NaN codes in
+ * A or B are outside the contract.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP,
+ * ERR_UNSUPPORTED, ERR_HIP.
+ */
+int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
+                    const uint8_t* A, const uint8_t* B,
+                    const float* scale_a, const float* scale_b,
+                    void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_gemm -- MXFP8 block-scaled GEMM.
+ *
+ * Source: the page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm 통합", section 1
+ * (one uint8 scale per 32 elements of K, scale tensor of shape (n, k // 32))
+ * and section 2 (the GEMM takes fp8 activations with their uint8 scales, the
+ * fp8 weight with its uint8 scales, and an output dtype).  A scale byte c
+ * stands for 2^(c - 127) (UE8M0).
+ *
+ *   D[m,n] = out( sum_j 2^(ea[m,j]-127) * 2^(eb[n,j]-127)
+ *                       * sum_{t<32} dec(A[m,32j+t]) * dec(B[n,32j+t]) )
+ * accumulated in fp32 on the scaled matrix-core instructions.  Accuracy as
+ * fp8_gemm_scaled with the block-scaled sum of |products| in the bound.
+ *
+ * A        device, E4M3 codes [m, k]          B   device, E4M3 codes [n, k]
+ * scale_a  device, UE8M0 codes [m, k/32]      scale_b device, UE8M0 codes [n, k/32]
+ * D        device, [m, n] of out_dtype, written
+ * k % 32 != 0 -> ERR_SHAPE.  m == 0 or n == 0: no-op.  k == 0: D = 0.
+ * Scale code 255 (NaN) and E4M3 NaN codes are outside the contract.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP, ERR_HIP.
+ */
+int mxfp8_gemm(int64_t m, int64_t n, int64_t k,
+               const uint8_t* A, const uint8_t* B,
+               const uint8_t* scale_a, const uint8_t* scale_b,
+               void* D, int out_dtype, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fp8g_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8G_H */

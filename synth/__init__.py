@@ -15,6 +15,8 @@ DeepGEMM call on the page "FP8 推理基础设施（五）：从 DeepGEMM 到 vL
 the MXFP8 setting of the page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm 통합".
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -59,15 +61,28 @@ def normal(key, start: int, count: int) -> np.ndarray:
     return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u[:, 1])
 
 
-def _rows(fn, key, R, C, row0=0, chunk=1 << 22):
-    """Fill an [R, C] float32 array row-major from a per-element generator."""
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _rows(fn, key, R, C, row0=0, chunk=1 << 18):
+    """Fill an [R, C] float32 array row-major from a per-element generator
+    (chunks in a thread pool; the values do not depend on the chunking)."""
     out = np.empty((R, C), dtype=np.float32)
     flat = out.reshape(-1)
     total = R * C
     base = row0 * C
-    for s in range(0, total, chunk):
+
+    def work(s):
         n = min(chunk, total - s)
         flat[s:s + n] = fn(key, base + s, n)
+
+    starts = range(0, total, chunk)
+    if len(starts) <= 1:
+        for s in starts:
+            work(s)
+    else:
+        with ThreadPoolExecutor(_WORKERS) as ex:
+            list(ex.map(work, starts))
     return out
 
 
@@ -134,11 +149,19 @@ def draw(w: Workload, side: str, rows: slice = None) -> np.ndarray:
         outlier = recipe.endswith("outlier")
         okey = stream_key(w.seed, S_OUTLIER)
         out = np.empty((n, C), dtype=np.float32)
-        for i in range(n):
+
+        def row(i):
             v = normal(key, (r0 + i) * C, C) * f[i]
             if outlier:
                 v = np.where(uniform(okey, (r0 + i) * C, C) < 0.01, v * 50.0, v)
             out[i] = v
+
+        if n > 1:
+            with ThreadPoolExecutor(_WORKERS) as ex:
+                list(ex.map(row, range(n)))
+        else:
+            for i in range(n):
+                row(i)
         return out
     if recipe == "blockpow2":
         g = block_pow2(w.seed, S_EA if side == "a" else S_EB, n, C, r0)

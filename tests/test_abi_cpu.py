@@ -1,0 +1,114 @@
+"""The C ABI on the CPU: the library loads, exports every declared function,
+and rejects bad arguments with the documented status before any HIP call.
+
+Pointers here are plain integers that are never dereferenced: every call in
+this file must return from the host-side checks (no device is touched).
+"""
+
+import ctypes
+
+import pytest
+
+import fp8_scaled_gemm_amd as fp8g
+
+OK, NULL, SHAPE, ALIGN, DTYPE, OVERLAP, UNSUPPORTED, HIP = range(8)
+P = 0x100000          # a fake, 16-byte aligned "device" address
+S = 0                 # null stream
+
+
+def P_(off):
+    return ctypes.c_void_p(P + off)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fp8g.load()
+
+
+def test_exports_every_header_function(lib):
+    names = fp8g.header_functions()
+    assert set(names) == {"fp8_quantize_rowwise", "fp8_gemm_scaled", "mxfp8_gemm", "fp8g_status_string"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert fp8g.status_string(st)
+    assert fp8g.status_string(99) == "unknown status"
+
+
+def gemm(lib, fn, m, n, k, A=P_(0), B=P_(1 << 30), sa=P_(2 << 30), sb=P_(3 << 30), D=P_(4 << 30), out=0):
+    return getattr(lib, fn)(m, n, k, A, B, sa, sb, D, out, ctypes.c_void_p(S))
+
+
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm"])
+def test_gemm_argument_checks(lib, fn):
+    assert gemm(lib, fn, -1, 4, 64) == SHAPE
+    assert gemm(lib, fn, 4, -1, 64) == SHAPE
+    assert gemm(lib, fn, 4, 4, -32) == SHAPE
+    assert gemm(lib, fn, 4, 4, 64, out=2) == DTYPE
+    assert gemm(lib, fn, 4, 4, 64, out=-1) == DTYPE
+    assert gemm(lib, fn, 0, 4, 64) == OK           # empty output: no-op
+    assert gemm(lib, fn, 4, 0, 64) == OK
+    assert gemm(lib, fn, 0, 0, 0, A=None, B=None, sa=None, sb=None, D=None) == OK
+    assert gemm(lib, fn, 4, 4, 64, D=None) == NULL
+    assert gemm(lib, fn, 4, 4, 64, A=None) == NULL
+    assert gemm(lib, fn, 4, 4, 64, B=None) == NULL
+    assert gemm(lib, fn, 4, 4, 64, sa=None) == NULL
+    assert gemm(lib, fn, 4, 4, 64, sb=None) == NULL
+    assert gemm(lib, fn, 4, 4, 64, A=P_(8)) == ALIGN
+    assert gemm(lib, fn, 4, 4, 64, B=P_((1 << 30) + 4)) == ALIGN
+    assert gemm(lib, fn, 4, 4, 64, D=P_((4 << 30) + 2)) == ALIGN
+    assert gemm(lib, fn, 4, 4, 64, sa=P_((2 << 30) + 1)) == ALIGN
+    # D overlaps A / B / a scale array
+    assert gemm(lib, fn, 4, 4, 64, D=P_(0)) == OVERLAP
+    assert gemm(lib, fn, 4, 4, 64, D=P_((1 << 30) + 16)) == OVERLAP
+    assert gemm(lib, fn, 4, 4, 64, D=P_((3 << 30) - 16)) == OVERLAP
+    # adjacent but not overlapping is fine up to the launch, which fails without a GPU
+    assert gemm(lib, fn, 4, 4, 64, D=P_(4 * 64)) in (OK, HIP)
+
+
+def test_mx_k_must_be_multiple_of_32(lib):
+    for k in (16, 48, 33, 1):
+        assert gemm(lib, "mxfp8_gemm", 4, 4, k) == SHAPE
+
+
+def test_scaled_k_must_be_multiple_of_16(lib):
+    for k in (8, 24, 33, 1):
+        assert gemm(lib, "fp8_gemm_scaled", 4, 4, k) == UNSUPPORTED
+
+
+def test_k_zero_needs_no_operands(lib):
+    # the empty sum: A and B may be NULL; the call proceeds to the launch
+    assert gemm(lib, "fp8_gemm_scaled", 4, 4, 0, A=None, B=None) in (OK, HIP)
+
+
+def test_huge_sizes_rejected(lib):
+    assert gemm(lib, "fp8_gemm_scaled", 1 << 40, 1 << 40, 1 << 20) == UNSUPPORTED
+
+
+def quant(lib, x=P_(0), rows=8, cols=64, q=P_(1 << 30), s=P_(2 << 30)):
+    return lib.fp8_quantize_rowwise(x, rows, cols, q, s, ctypes.c_void_p(S))
+
+
+def test_quantize_argument_checks(lib):
+    assert quant(lib, rows=-1) == SHAPE
+    assert quant(lib, cols=-1) == SHAPE
+    assert quant(lib, rows=0, x=None, q=None, s=None) == OK
+    assert quant(lib, s=None) == NULL
+    assert quant(lib, x=None) == NULL
+    assert quant(lib, q=None) == NULL
+    assert quant(lib, x=P_(4)) == ALIGN
+    assert quant(lib, q=P_((1 << 30) + 1)) == ALIGN
+    assert quant(lib, s=P_((2 << 30) + 8)) == ALIGN
+    assert quant(lib, q=P_(64)) == OVERLAP                    # q inside x
+    assert quant(lib, s=P_((1 << 30) + 16)) == OVERLAP        # scale inside q
+    assert quant(lib, cols=0, x=None, q=None) in (OK, HIP)    # empty rows: only scales written
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fp8g, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fp8g, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fp8g.load()

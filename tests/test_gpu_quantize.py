@@ -1,0 +1,138 @@
+"""GPU parity of fp8_quantize_rowwise: bit-exact codes and scales vs the oracle."""
+
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import oracle_quantize_rows, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run(fp8g, x):
+    q, s = fp8g.fp8_quantize_rowwise(to_dev(x))
+    return to_host(q), to_host(s)
+
+
+def check_rows(fp8g, x, what):
+    say("quantize", what, x.shape)
+    q, s = run(fp8g, x)
+    qr, sr = oracle_quantize_rows(x)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32)), what + ": scales differ"
+    if not np.array_equal(q, qr):
+        r, c = np.argwhere(q != qr)[0]
+        raise AssertionError("%s: %d codes differ; first at (%d,%d): x=%r gpu=%02x oracle=%02x"
+                             % (what, int((q != qr).sum()), r, c, x[r, c], q[r, c], qr[r, c]))
+
+
+# shapes exercise every kernel variant: vector rows of 1..32 float4 per lane,
+# the two-pass vector path (> 8192 per row), and the element-wise path (cols % 4 != 0)
+SHAPES = [(1, 4), (3, 16), (5, 60), (7, 256), (9, 260), (128, 512), (6, 1000), (4, 2048), (33, 4096),
+          (130, 8192), (3, 8196), (4, 10000), (5, 257), (9, 1002), (2, 1), (3, 3), (64, 4099)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_quantize_shapes(gpu_lib, rows, cols):
+    w = synth.Workload("q", rows, rows, cols, "a", "rowfactor_outlier", "normal", "rowwise", 11)
+    check_rows(gpu_lib, synth.draw(w, "a"), "rowfactor_outlier")
+
+
+def edge_rows(cols=64):
+    t = 2.0 ** -149
+    rows = [
+        np.zeros(cols),                                       # all zero -> s = 0, +0 codes
+        np.where(np.arange(cols) % 2 == 0, 0.0, -0.0),        # signed zeros
+        np.r_[t, -t, np.zeros(cols - 2)],                     # amax/448 underflows -> s = 0, signed zeros
+        np.r_[1075 * t, 300 * t, -1075 * t, np.zeros(cols - 3)],   # subnormal s: saturation path
+        np.r_[896.0, 1.0, -3.0, 0.5, 2.0 ** -8, 15 * 2.0 ** -9, -2.0 ** -12, np.zeros(cols - 7)],
+        np.r_[-5.0, np.zeros(cols - 1)],                      # single nonzero, negative
+        np.linspace(-448, 448, cols),                         # s = 1: plain cast incl. exact grid points
+        np.r_[448.0, (np.arange(1, cols) + 0.5) * 2.0 ** -9],  # subnormal-range midpoints at s = 1
+        np.full(cols, 3.0e38),                                # huge, all equal
+        np.r_[1e-38, 3e-39, -7e-40, np.zeros(cols - 3)],      # amax is itself near/below fp32 normal min
+        np.r_[2.0 ** 100, 2.0 ** 50, -1.0, np.zeros(cols - 3)],  # wide dynamic range: tiny codes flush to 0
+    ]
+    return np.array(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("cols", [64, 67])
+def test_quantize_edge_rows(gpu_lib, cols):
+    check_rows(gpu_lib, edge_rows(cols), "edge rows, cols=%d" % cols)
+
+
+def test_quantize_empty(gpu_lib):
+    import torch
+    x = torch.zeros((0, 16), dtype=torch.float32, device="cuda")
+    q, s = gpu_lib.fp8_quantize_rowwise(x)
+    assert q.shape == (0, 16) and s.shape == (0,)
+    x = torch.zeros((3, 0), dtype=torch.float32, device="cuda")
+    s = torch.full((3,), 7.0, device="cuda")
+    q, s = gpu_lib.fp8_quantize_rowwise(x, scale=s)
+    assert to_host(s).tolist() == [0.0, 0.0, 0.0]
+
+
+def _thresholds():
+    vals = []
+    for line in open(os.path.join(GOLDEN, "e4m3_thresholds.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            vals.append(int(line.split()[1], 16))
+    assert len(vals) == 126
+    return vals
+
+
+def test_cast_every_fp32_pattern_up_to_448(gpu_lib):
+    """Rows [448 x4, p .. p+8187] give s = 1, so q = cast(x) exactly: every
+    non-negative fp32 pattern up to 448, and its negative, through the main
+    (register-resident, 8192-column) kernel.  Expected codes come from the
+    oracle's thresholds (tests/golden/e4m3_thresholds.txt)."""
+    import torch
+    thr = torch.tensor(_thresholds(), dtype=torch.int64, device="cuda")
+    top = int(np.array([448.0], np.float32).view(np.uint32)[0])
+    per_row = 8188
+    rows = 16384
+    head = torch.full((rows, 4), 448.0, dtype=torch.float32, device="cuda")
+    start = 0
+    while start <= top:
+        n = min(rows * per_row, top + 1 - start)
+        r = (n + per_row - 1) // per_row
+        bits = torch.arange(start, start + r * per_row, dtype=torch.int64, device="cuda")
+        bits = torch.clamp(bits, max=top)
+        x = torch.cat([head[:r], bits.to(torch.int32).view(torch.float32).view(r, per_row)], dim=1).contiguous()
+        want = torch.bucketize(bits, thr, right=True).to(torch.uint8).view(r, per_row)
+        for sign in (1.0, -1.0):
+            say("exhaustive cast", hex(start), "sign", sign)
+            q, s = gpu_lib.fp8_quantize_rowwise(x * sign)
+            assert bool((s == 1.0).all())
+            qc = q.view(torch.uint8)
+            assert bool((qc[:, :4] == (0x7E if sign > 0 else 0xFE)).all())
+            exp = want if sign > 0 else (want | 0x80)
+            bad = (qc[:, 4:] != exp)
+            if bool(bad.any()):
+                i = int(torch.nonzero(bad.view(-1))[0])
+                raise AssertionError("pattern 0x%08x sign %+d: gpu %02x oracle %02x"
+                                     % (int(bits[i]), int(sign), int(qc[:, 4:].reshape(-1)[i]),
+                                        int(exp.reshape(-1)[i])))
+        start += n
+
+
+@pytest.mark.parametrize("side,rows", [("a", None), ("b", slice(0, 4096))])
+def test_quantize_ffn_up_operands(gpu_lib, side, rows):
+    """The 8192x22016x8192 FFN-up workload: activations (8192 x 8192, per-row
+    log-uniform factors and x50 outliers) in full; weights (N(0, 0.02)) on the
+    first 4096 channels."""
+    w = synth.WORKLOADS["c4_ffn_up_8192x22016x8192"]
+    check_rows(gpu_lib, synth.draw(w, side, rows), "ffn_up side " + side)
+
+
+def test_quantize_deterministic(gpu_lib):
+    w = synth.WORKLOADS["c3_8192x2048x8192"]
+    x = to_dev(synth.draw(w, "a", slice(0, 512)))
+    q1, s1 = gpu_lib.fp8_quantize_rowwise(x)
+    q2, s2 = gpu_lib.fp8_quantize_rowwise(x)
+    import torch
+    assert torch.equal(q1.view(torch.uint8), q2.view(torch.uint8)) and torch.equal(s1, s2)
