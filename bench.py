@@ -52,13 +52,28 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=None,
                    help="JSON file with measured HBM bytes per GEMM launch (from rocprofv3 counters)")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="only run a plain device-to-device copy of this many bytes (calibrates the "
+                        "HBM byte counters of a profiler run against a known size)")
     return p.parse_args()
 
 
-def cpu_baseline_ffn_up(w, m_s=512, n_s=4096):
+def copy_only(nbytes, reps=5):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_bytes": nbytes, "seconds": dt, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
+
+
+def cpu_baseline_ffn_up(w, m_s=2048, n_s=16384):
     """The oracle on a sample: rows 0..m_s of the activations, rows 0..n_s of the
     weights: quantize both (row-wise) and form the m_s x n_s block of D."""
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import gemm, quant
     XA = synth.draw(w, "a", slice(0, m_s))
     XB = synth.draw(w, "b", slice(0, n_s))
@@ -81,7 +96,7 @@ def cpu_baseline_ffn_up(w, m_s=512, n_s=4096):
                       % (m_s, n_s, m_s, n_s, w.K, m_s, n_s, w.K)}
 
 
-def cpu_baseline_mx(w, m_s=512, n_s=2048):
+def cpu_baseline_mx(w, m_s=2048, n_s=8192):
     from oracle import gemm, quant
     XA = synth.draw(w, "a", slice(0, m_s))
     XB = synth.draw(w, "b", slice(0, n_s))
@@ -119,6 +134,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_only(args.copy_bytes)
+        return
     fp8g.load()
     w = synth.WORKLOADS[WORKLOADS[args.workload]]
     dev = torch.device("cuda", 0)
