@@ -51,7 +51,8 @@ def parse():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=None,
-                   help="JSON file with measured HBM bytes per GEMM launch (from rocprofv3 counters)")
+                   help="counter summary with the measured HBM bytes per GEMM launch (default: the one "
+                        "under profiles/ for the workload)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run a plain device-to-device copy of this many bytes (calibrates the "
                         "HBM byte counters of a profiler run against a known size)")
@@ -71,7 +72,7 @@ def copy_only(nbytes, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "seconds": dt, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
 
 
-def cpu_baseline_ffn_up(w, m_s=2048, n_s=16384):
+def cpu_baseline_ffn_up(w, m_s=4096, n_s=16384):
     """The oracle on a sample: rows 0..m_s of the activations, rows 0..n_s of the
     weights: quantize both (row-wise) and form the m_s x n_s block of D."""
     from oracle import gemm, quant
@@ -110,6 +111,37 @@ def cpu_baseline_mx(w, m_s=2048, n_s=8192):
             "seconds": round(dt, 3),
             "sample": "oracle MX quantize of rows 0..%d / 0..%d, then the %dx%dx%d block of D in float64"
                       % (m_s, n_s, m_s, n_s, w.K)}
+
+
+TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic.txt",
+                 "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt"}
+
+
+def source_digest():
+    """sha256 of the GEMM kernel source: counters taken on another version of it
+    do not describe the kernel being timed."""
+    import hashlib
+    with open(os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(path):
+    """HBM bytes per GEMM launch from a counter summary ('key: value' lines), or
+    None when the file is missing or was taken on a different kernel source."""
+    if not path or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        log("traffic summary %s was taken on another kernel source: traffic = null" % path)
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _blas_threads():
@@ -190,9 +222,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_us = per_kernel["gemm"]
     achieved = flops / (gemm_us * 1e-6) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("gemm_bytes_per_launch")
+    traffic = read_traffic(args.traffic or os.path.join(ROOT, TRAFFIC_FILES[args.workload]))
     line = {
         "metric": "FP8 GEMM TFLOP/s and % of FP8 MFMA peak at MxNxK=8192x22016x8192"
                   if args.workload == "ffn_up" else "MXFP8 GEMM TFLOP/s at 4096x14336x4096",
