@@ -24,11 +24,12 @@ __device__ __forceinline__ uint8_t e4m3_one(float a) {
     return (uint8_t)(e4m3_pack4(a, 0.0f, 0.0f, 0.0f) & 0xFFu);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite and infinite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> two bf16 (round to nearest even) packed low / high, with
+// the gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -13,38 +13,41 @@
 //
 // Tiling: a 256-thread workgroup (4 waves, 2x2) owns a 256x256 output tile;
 // each wave owns 128x128 = 4x4 blocks of the 32x32 matrix-core tile (256 fp32
-// accumulators per lane).  K is walked in 64-byte stages, one
-// V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block per stage; mode (a) passes the
+// accumulators per lane).  K is walked in 64-byte steps, one
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block per step; mode (a) passes the
 // neutral scale code 127 (2^0) and applies sa, sb in the epilogue, mode (b)
 // passes the operands' block scales.
 //
-// Persistent workgroups: one per CU, each walking a list of tiles.  Its stages
-// form one continuous stream across its tiles, so the loads of the next tile
-// are in flight while the current tile's epilogue runs.
+// Persistent workgroups: one per CU, each walking a list of tiles.  Its
+// stages (128 bytes of K, two steps) form one stream across its tiles, so the
+// loads of the next tile are in flight while the current tile's epilogue runs.
 //
 // Operand staging: direct global -> LDS loads (buffer_load_dwordx4 ... lds;
-// lane L of a wave writes LDS bytes [M0 + 16L, M0 + 16L + 16)), four LDS stage
-// buffers, issued three stages ahead.  No registers hold staged data and no
-// LDS-write instructions are needed.  The compiler cannot track these loads
+// lane L of a wave writes LDS bytes [M0 + 16L, M0 + 16L + 16)).  A stage moves
+// 128 bytes of every row: whole 128-byte lines, which the memory system serves
+// at twice the rate of 64-byte pieces of rows (measured: 66 vs 33 bytes per
+// clock per CU from L2 for rows 8 KB apart).  Each operand of a stage (256 rows
+// x 128 B = 32 KB) is one "item" in a ring of NSLOT LDS slots (5 x 32 KB =
+// 160 KB; mode (b) with whole scale dwords uses 4 slots of 33 KB).  One item
+// is loaded per K step, its 8 loads spread over that step's matrix-core
+// instructions, NSLOT-1 items ahead.  The compiler cannot track these loads
 // (it would wait for all of them before every LDS read), so they are issued
-// from inline assembly (they write LDS only, no registers) and the kernel
-// waits for them itself: before the barrier of stage g it waits until only the
-// loads issued after stage g+1's remain (vector-memory loads complete in
-// order, so a count of outstanding loads identifies the stage).
+// from inline assembly and the kernel waits for them itself; vector-memory
+// loads complete in order, so a count of outstanding loads identifies the
+// item.  Loads past the end of a panel (rows past M or N, bytes past K) read 0
+// (buffer range check on voffset + soffset).
 //
-// LDS layout per stage: A then B, 256 rows of 64 bytes (four 16-byte chunks);
-// logical chunk c of row r sits in slot c ^ ((r >> 2) & 3).  A 128-bit read
-// serves 16 lanes per LDS cycle (64 banks): 16 consecutive rows at one
-// logical chunk hit 16 distinct 16-byte bank groups.  The swizzle is applied
-// on the global side: lane L of a load fills slot L % 4 of row L / 4 and so
-// fetches chunk (L % 4) ^ ((L / 16) & 3) of that row.  Mode (b) adds one
-// dword of scales (4 blocks, a stage pair) per row and operand.
+// LDS layout of a slot: 256 rows of 128 bytes (eight 16-byte chunks); logical
+// chunk c of row r sits in slot c ^ ((r >> 1) & 7).  A 128-bit read serves 16
+// lanes per LDS cycle (64 banks, 256 bytes): 16 consecutive rows at one logical
+// chunk fall in 16 distinct 16-byte bank groups.  A load instruction fills 8
+// rows: lane L takes slot L % 8 of row L / 8 and fetches the chunk stored there.
 //
 // The matrix core reads a lane's 32 operand bytes as two 16-byte halves:
 // bytes 0-15 belong to K block 0 of the 64-wide step and bytes 16-31 to block
-// 1; lanes 32-63 hold the upper 16 of each block.  So a lane takes chunks lhi
-// and 2 + lhi of its row, and the scale of block 0 / 1 of the step comes from
-// lanes 0-31 / 32-63.
+// 1; lanes 32-63 hold the upper 16 of each block.  So for step h of a stage a
+// lane takes chunks 4h + lhi and 4h + 2 + lhi of its row, and the scale of
+// block 0 / 1 of the step comes from lanes 0-31 / 32-63.
 //
 // Operand roles: the matrix-core "A" operand is fed from B's rows (n) and the
 // "B" operand from A's rows (m), so each lane's accumulator block holds one m
@@ -73,19 +76,29 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256;        // tile rows (m)
 constexpr int BN = 256;        // tile cols (n)
-constexpr int BK = 64;         // bytes of K per stage (one matrix-core step)
+constexpr int BK = 128;        // bytes of K per stage (two matrix-core steps)
+constexpr int KSTEP = 64;      // bytes of K per matrix-core step
 constexpr int NTHREADS = 256;
 constexpr int WT = 128;        // wave tile edge
 constexpr int NB = WT / 32;    // 32x32 blocks per wave-tile edge
 constexpr int NUM_XCD = 8;
 constexpr int GROUP_M = 8;
-constexpr int NSTAGE = 4;      // LDS stage buffers; loads run NSTAGE-1 stages ahead
 
-constexpr int OP_BYTES = BM * BK;                 // 16 KB: one operand, one stage
-constexpr int SCALE_BYTES = BM * 4;               // MX: one dword (4 blocks) per row, per operand
-constexpr int STAGE_BYTES = 2 * OP_BYTES + 2 * SCALE_BYTES;   // 34 KB
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 136 KB
-constexpr int DMA_PER_OP = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 4
+constexpr int OP_BYTES = BM * BK;      // 32 KB: one operand of one stage (an "item")
+constexpr int SCALE_BYTES = BM * 4;    // mode (b): the stage's 4 block scales of every row, one dword
+constexpr int DMA_PER_ITEM = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 8
+
+// Ring geometry per kernel variant: mode (b) with whole scale dwords keeps each
+// item's scales beside it (4 slots of 33 KB); otherwise 5 slots of 32 KB.
+template <bool MX, bool KTAIL>
+struct Ring {
+    static constexpr bool SCALES = MX && !KTAIL;
+    static constexpr int NSLOT = SCALES ? 4 : 5;
+    static constexpr int SLOT = OP_BYTES + (SCALES ? SCALE_BYTES : 0);
+    static constexpr int LDS = NSLOT * SLOT;
+    static constexpr int LOADS = DMA_PER_ITEM + (SCALES ? 1 : 0);   // load instructions per item and wave
+};
+static_assert(Ring<false, false>::LDS <= 160 * 1024 && Ring<true, false>::LDS <= 160 * 1024, "LDS");
 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
 
@@ -167,17 +180,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;   // LDS byte address of the stage buffers
 
-    // ---- loads of the stream's stages, in order, into LDS buffer g % NSTAGE,
-    // NSTAGE stages ahead of the stage being computed.  A cursor (tile, stage)
-    // walks the stream; descriptors change once per tile.  Past the end of the
-    // stream the last stage is loaded again into a free buffer (never read), so
-    // every stage issues the same number of loads.
-    // lane L of wave w fills row 16*(4p + w) + L/4, slot L%4, for p = 0..3
-    const uint32_t dma_row = (uint32_t)(16 * wave + (lane >> 2));
-    const uint32_t dma_voff = dma_row * (uint32_t)K + (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-    // MX scales: dword DMA, lane L of wave w fills row 64*w + L (4 blocks = one stage pair)
+    // ---- loads.  Item i of the stream is operand i & 1 (A, B) of stream stage
+    // i >> 1; it goes to LDS slot i % NSLOT.  A cursor (tile, stage, operand)
+    // walks the items; descriptors change once per tile.  Past the end of the
+    // stream the last stage is loaded again (never read), so every K step
+    // issues the same number of loads.
+    using R = Ring<MX, KTAIL>;
+    constexpr int NSLOT = R::NSLOT, SLOT = R::SLOT, LI = R::LOADS;
+    // lane L of wave w, instruction p fills row 32p + 8w + L/8, slot L%8, which
+    // holds logical chunk (L%8) ^ ((row >> 1) & 7) = (L%8) ^ ((4w + L/16) & 7)
+    const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
+    const uint32_t dma_voff = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)K + dma_chunk * 16u;
+    // mode (b) scales: dword loads, lane L of wave w fills row 64w + L
     const uint32_t sdma_voff = (uint32_t)(64 * wave + lane) * (uint32_t)nblk;
-    int ij = 0, is = 0, ig = 0;                        // cursor: tile, stage in tile, stream stage
+    constexpr uint32_t OOB_OFF = 0x80000000u;   // past any panel (panels are < 2^31 bytes)
+    int ij = 0, is = 0, iop = 0, ii = 0, islot = 0;   // cursor: tile, stage in tile, operand, item, its slot
     __amdgpu_buffer_rsrc_t rsA, rsB, rsEA, rsEB;
     auto cursor_tile = [&]() __attribute__((always_inline)) {
         const TileCoord tc = tile_of(min(ij, my_tiles - 1));
@@ -190,72 +207,78 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             rsEB = panel(eb + (int64_t)n0 * nblk, rows_b * (uint32_t)nblk);
         }
     };
-    // load q of the cursor's stage: q = 2p (+1) is row group p of A (B); in mode
-    // (b) q = 8 (9) is the scale dword of A (B) for the stage's pair, which every
-    // stage of the pair loads into its own buffer
+    // load q (0..LI-1) of the cursor's item
     auto dma_item = [&](int q) __attribute__((always_inline)) {
-        const int s_ld = ig < NS ? is : nk - 1;        // past the end: reload the last stage
-        const uint32_t sbuf = lds0 + (uint32_t)((ig % NSTAGE) * STAGE_BYTES);
-        if (q < 2 * DMA_PER_OP) {
-            const int p = q >> 1;
-            const uint32_t so = uniform((uint32_t)(s_ld * BK) + (uint32_t)(64 * p) * (uint32_t)K);
-            dma16(uniform(sbuf + (uint32_t)((q & 1) * OP_BYTES + p * 4096 + wave * 1024)), dma_voff,
-                  (q & 1) ? rsB : rsA, so);
-        } else if constexpr (MX && !KTAIL) {
-            const uint32_t so = uniform((uint32_t)(2 * (s_ld & ~1)));
-            dma4(uniform(sbuf + (uint32_t)(2 * OP_BYTES + (q & 1) * SCALE_BYTES + wave * 256)), sdma_voff,
-                 (q & 1) ? rsEB : rsEA, so);
+        const int s_ld = (ii < 2 * NS) ? is : nk - 1;   // past the end: reload the last stage
+        const uint32_t sbuf = lds0 + (uint32_t)(islot * SLOT);
+        const uint32_t k0 = (uint32_t)(s_ld * BK);
+        if (q < DMA_PER_ITEM) {
+            uint32_t voff = dma_voff;
+            if constexpr (KTAIL) {
+                // bytes past K (the next row's, or past the panel) must read as 0
+                if (k0 + dma_chunk * 16u >= (uint32_t)K) voff = OOB_OFF;
+            }
+            const uint32_t so = uniform(k0 + (uint32_t)(32 * q) * (uint32_t)K);
+            dma16(uniform(sbuf + (uint32_t)((4 * q + wave) * 1024)), voff, iop ? rsB : rsA, so);
+        } else if constexpr (R::SCALES) {
+            dma4(uniform(sbuf + (uint32_t)(OP_BYTES + wave * 256)), sdma_voff, iop ? rsEB : rsEA,
+                 uniform((uint32_t)(4 * s_ld)));
         }
     };
     auto advance = [&]() __attribute__((always_inline)) {
-        ++ig;
-        if (++is == nk) {
-            is = 0;
-            ++ij;
-            cursor_tile();
+        ++ii;
+        islot = (islot + 1 == NSLOT) ? 0 : islot + 1;
+        if (++iop == 2) {
+            iop = 0;
+            if (++is == nk) {
+                is = 0;
+                ++ij;
+                cursor_tile();
+            }
         }
     };
 
-    // loads per stage
-    constexpr int LOADS = 2 * DMA_PER_OP + ((MX && !KTAIL) ? 2 : 0);
-
-    // ---- fragment reads (stage buffer, this lane's rows, chunks lhi and 2+lhi)
-    const uint32_t key = (uint32_t)((l32 >> 2) & 3);
-    const uint32_t frag_a0 = (uint32_t)((wm * WT + l32) * BK) + (((uint32_t)lhi ^ key) << 4);
-    const uint32_t frag_a1 = (uint32_t)((wm * WT + l32) * BK) + (((uint32_t)(2 + lhi) ^ key) << 4);
-    const uint32_t frag_b0 = frag_a0 - (uint32_t)(wm * WT * BK) + (uint32_t)(OP_BYTES + wn * WT * BK);
-    const uint32_t frag_b1 = frag_a1 - (uint32_t)(wm * WT * BK) + (uint32_t)(OP_BYTES + wn * WT * BK);
-    auto frag = [&](int g, uint32_t off0, uint32_t off1, int i) __attribute__((always_inline)) -> v8i {
-        const uint8_t* sbuf = smem + (g % NSTAGE) * STAGE_BYTES;
-        const v4u x0 = *reinterpret_cast<const v4u*>(sbuf + off0 + i * 32 * BK);
-        const v4u x1 = *reinterpret_cast<const v4u*>(sbuf + off1 + i * 32 * BK);
+    // ---- fragment reads: step h of the stage whose items sit in LDS slots
+    // sa_off (A) and sb_off (B); this lane's rows, chunks 4h + lhi and 4h + 2 + lhi
+    const uint32_t key = (uint32_t)((l32 >> 1) & 7);
+    const uint32_t frag_a = (uint32_t)((wm * WT + l32) * BK);
+    const uint32_t frag_b = (uint32_t)((wn * WT + l32) * BK);
+    const uint32_t c0 = ((uint32_t)lhi ^ key) << 4, c1 = ((uint32_t)(2 + lhi) ^ key) << 4;
+    auto frag = [&](uint32_t slot_off, uint32_t row_off, int h, int i) __attribute__((always_inline)) -> v8i {
+        const uint8_t* p = smem + slot_off + row_off + i * 32 * BK;
+        const v4u x0 = *reinterpret_cast<const v4u*>(p + (c0 ^ (uint32_t)(64 * h)));
+        const v4u x1 = *reinterpret_cast<const v4u*>(p + (c1 ^ (uint32_t)(64 * h)));
         return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
+    // slot index + k, modulo NSLOT (k < NSLOT)
+    auto slot_add = [&](int slot, int k) __attribute__((always_inline)) -> int {
+        return (slot + k >= NSLOT) ? slot + k - NSLOT : slot + k;
+    };
 
-    // ---- MX scales for stage g: per lane and row block, the scale byte of this
-    // lane half's block in byte 0 (so the matrix core always reads byte 0).
-    // Non-tail: one dword (blocks 4p..4p+3, a stage pair) per row in the LDS
-    // scale area of the stage.  Tail (rows of nblk bytes, not a
-    // multiple of 4): bytes from global, 2^0 past the row end.  Rows past M / N
-    // read 0 (their data is zero too).
-    auto read_scales = [&](int g, int s, uint32_t* xa, uint32_t* xb) __attribute__((always_inline)) {
+    // ---- mode (b) scales for step h of stream stage g: per lane and row block,
+    // the scale byte of this lane half's block in byte 0 (the matrix core reads
+    // byte 0).  With whole scale dwords: the dword of the stage (blocks 4s..4s+3)
+    // sits beside each item in LDS.  Otherwise (rows of nblk bytes, not a
+    // multiple of 4): unconditional byte loads from global, 2^0 past the row
+    // end; rows past M / N read 0 (their data is zero too).
+    auto read_scales = [&](int g, int h, uint32_t sa_off, uint32_t sb_off, uint32_t* xa, uint32_t* xb)
+                           __attribute__((always_inline)) {
         if constexpr (MX) {
-            const uint32_t sh = (uint32_t)(8 * (2 * (s & 1) + lhi));
-            if constexpr (!KTAIL) {
-                const uint8_t* sc = smem + (g % NSTAGE) * STAGE_BYTES + 2 * OP_BYTES;
+            if constexpr (R::SCALES) {
+                const uint32_t sh = (uint32_t)(8 * (2 * h + lhi));
+                const uint8_t* sca = smem + sa_off + OP_BYTES;
+                const uint8_t* scb = smem + sb_off + OP_BYTES;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    xa[i] = *reinterpret_cast<const uint32_t*>(sc + (wm * WT + i * 32 + l32) * 4) >> sh;
-                    xb[i] = *reinterpret_cast<const uint32_t*>(sc + SCALE_BYTES + (wn * WT + i * 32 + l32) * 4) >> sh;
+                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32) * 4) >> sh;
+                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32) * 4) >> sh;
                 }
             } else {
-                // unconditional buffer loads (no lane-divergent branch near the
-                // matrix-core steps); rows past M / N read 0 from past the panel
                 const TileCoord tc = tile_of(g / nk);
                 const int m0 = tc.tm * BM, n0 = tc.tn * BN;
                 const __amdgpu_buffer_rsrc_t pa = panel(ea + (int64_t)m0 * nblk, (uint32_t)min(BM, M - m0) * (uint32_t)nblk);
                 const __amdgpu_buffer_rsrc_t pb = panel(eb + (int64_t)n0 * nblk, (uint32_t)min(BN, N - n0) * (uint32_t)nblk);
-                const int kb = 2 * s + lhi;                 // this lane half's block of stage s
+                const int kb = 4 * (g % nk) + 2 * h + lhi;   // this lane half's block
                 const bool in = kb < nblk;
                 const uint32_t kc = (uint32_t)min(kb, nblk - 1);
 #pragma unroll
@@ -266,28 +289,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                         pb, (uint32_t)(wn * WT + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
                     xa[i] = in ? va : 127u;
                     xb[i] = in ? vb : 127u;
-                }
-            }
-        }
-    };
-
-    // ---- K tail: the last stage of a tile holds chunks past K (the next row's
-    // bytes, or zeros past the panel): zero them in LDS once the stage landed.
-    auto fix_tail = [&](int g) __attribute__((always_inline)) {
-        if constexpr (KTAIL) {
-            const int s = g % nk;
-            if (s == nk - 1) {
-                uint8_t* sbuf = smem + (g % NSTAGE) * STAGE_BYTES;
-                // 512 rows (A then B) x 4 chunks; thread tid handles chunk tid & 3 of rows tid/4 + 64 i
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = (tid >> 2) + 64 * i;         // 0..511
-                    const int c = tid & 3;
-                    if (s * BK + c * 16 >= K) {
-                        const int rr = row & 255;
-                        *reinterpret_cast<v4u*>(sbuf + (row >> 8) * OP_BYTES + rr * BK +
-                                                ((c ^ ((rr >> 2) & 3)) << 4)) = (v4u){0u, 0u, 0u, 0u};
-                    }
                 }
             }
         }
@@ -372,8 +373,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                             __builtin_amdgcn_raw_buffer_store_b128(w4, rsD, off, 0, 0);
                         } else {
                             typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-                            const v2u w2 = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
-                                            bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+                            const v2u w2 = {bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
                             __builtin_amdgcn_raw_buffer_store_b64(w2, rsD, off, 0, 0);
                         }
                     } else {
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                             if constexpr (OUT_F32)
                                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[t]), rsD, off, 0, 0);
                             else
-                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits(v[t]), rsD, off, 0, 0);
+                                __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16x2_bits(v[t], 0.0f), rsD, off, 0, 0);
                         }
                     }
                 }
@@ -404,69 +404,69 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     }
     if (NS == 0) return;
 
-    // ---- prologue: stages 0..NSTAGE-1 in flight; stage 0 landed and its fragments read
+    // ---- prologue: items 0 .. NSLOT-2 in flight; stage 0 (items 0, 1) landed
+    // and the fragments of its step 0 read
     cursor_tile();
-    for (int g = 0; g < NSTAGE; ++g) {
+    for (int i = 0; i < NSLOT - 1; ++i) {
 #pragma unroll
-        for (int q = 0; q < LOADS; ++q) dma_item(q);
+        for (int q = 0; q < LI; ++q) dma_item(q);
         advance();
     }
-    wait_vmcnt<(NSTAGE - 1) * LOADS>();
+    wait_vmcnt<(NSLOT - 3) * LI>();
     __syncthreads();
-    fix_tail(0);
-    if constexpr (KTAIL) __syncthreads();
 
-    // Fragment registers are double-buffered: stage g computes from one set
-    // while the other receives stage g+1's fragments.
+    // Fragment registers are double-buffered: step t computes from one set
+    // while the other receives step t+1's fragments.
     v8i fa0[NB], fb0[NB], fa1[NB], fb1[NB];
     uint32_t xa[NB] = {}, xb[NB] = {};
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        fa0[i] = frag(0, frag_a0, frag_a1, i);
-        fb0[i] = frag(0, frag_b0, frag_b1, i);
+        fa0[i] = frag(0, frag_a, 0, i);
+        fb0[i] = frag(SLOT, frag_b, 0, i);
     }
-    read_scales(0, 0, xa, xb);
+    read_scales(0, 0, 0, SLOT, xa, xb);
+    int rslot = 0;   // LDS slot of the current stage's A item (its B item is the next slot)
 
-    // ---- the stream.  Stage g (fragments and scales in registers):
+    // ---- one K step: step h of stream stage g (fragments and scales in registers).
     //   the 4 matrix-core steps of row block 0;
-    //   wait until stage g+1 landed (g+2, g+3 may be in flight) and sync: its
-    //   loads landed everywhere, and every wave's reads of buffer g % NSTAGE
-    //   (stage g's fragments, read during stage g-1) are done (the barrier
-    //   waits for outstanding LDS reads);
-    //   12 slots, each one matrix-core step plus one load of stage g+NSTAGE
-    //   into buffer g % NSTAGE and two 16-byte LDS reads of stage g+1's
-    //   fragments into the other register set.  Spreading the loads keeps the
-    //   address unit from blocking the matrix-core steps behind a burst of
-    //   loads from all four waves.
-    auto stage = [&](v16f (&acc)[NB][NB], int g, int s, const v8i* fa, const v8i* fb, v8i* na,
+    //   h == 1 only: wait until stage g+1's items landed (items past them may be
+    //   in flight) and sync: they landed for every wave, and every wave's reads
+    //   of stage g's items (done during step 0) are finished (the barrier waits
+    //   for outstanding LDS reads), so their slots may be refilled;
+    //   12 slots, each one matrix-core step plus one load of the item NSLOT-1
+    //   ahead (into the slot of the item just before this step's) and two
+    //   16-byte LDS reads of the next step's fragments into the other register
+    //   set.  Spreading the loads keeps the address unit from blocking the
+    //   matrix-core steps behind a burst of loads from all four waves.
+    auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, const v8i* fa, const v8i* fb, v8i* na,
                      v8i* nbf) __attribute__((always_inline)) {
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(NSTAGE - 2) * LOADS>();
-        __syncthreads();
-        if constexpr (KTAIL) {
-            fix_tail(g + 1);
+        if (h == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(NSLOT - 4) * LI>();
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        const int g1 = g + 1;
-        const int s1 = (s + 1 == nk) ? 0 : s + 1;
+        const int gn = h ? g + 1 : g, hn = h ^ 1;
+        const int na_slot = h ? slot_add(rslot, 2) : rslot;   // slots of the items read next
+        const uint32_t sa_off = (uint32_t)(na_slot * SLOT), sb_off = (uint32_t)(slot_add(na_slot, 1) * SLOT);
         uint32_t nxa[NB], nxb[NB];
 #pragma unroll
         for (int k = 0; k < 12; ++k) {
             const int i = 1 + k / 4, jb = k % 4;
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
-            if (k < LOADS) dma_item(k);
+            if (k < LI) dma_item(k);
             // reads in order of first use: row block 0 of B, the four of A, then B 1..3
-            if (k == 0) nbf[0] = frag(g1, frag_b0, frag_b1, 0);
-            if (k >= 1 && k <= 4) na[k - 1] = frag(g1, frag_a0, frag_a1, k - 1);
-            if (k >= 5 && k <= 7) nbf[k - 4] = frag(g1, frag_b0, frag_b1, k - 4);
-            if (k == 8) read_scales(g1, s1, nxa, nxb);
+            if (k == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
+            if (k >= 1 && k <= 4) na[k - 1] = frag(sa_off, frag_a, hn, k - 1);
+            if (k >= 5 && k <= 7) nbf[k - 4] = frag(sb_off, frag_b, hn, k - 4);
+            if (k == 9) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
             __builtin_amdgcn_sched_barrier(0);
         }
         advance();
-        // keep this stage's operand registers allocated to its end
+        if (h) rslot = na_slot;
+        // keep this step's operand registers allocated to its end
 #pragma unroll
         for (int i = 0; i < NB; ++i) asm volatile("" : : "v"(fa[i]), "v"(fb[i]));
 #pragma unroll
@@ -483,19 +483,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-        int s = 0;
-        for (; s + 1 < nk; s += 2, g += 2) {
-            stage(acc, g, s, fa0, fb0, fa1, fb1);
-            stage(acc, g + 1, s + 1, fa1, fb1, fa0, fb0);
-        }
-        if (s < nk) {   // odd stage count: the last stage alone, then realign the register sets
-            stage(acc, g, s, fa0, fb0, fa1, fb1);
-            ++g;
-#pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                fa0[i] = fa1[i];
-                fb0[i] = fb1[i];
-            }
+        for (int s = 0; s < nk; ++s, ++g) {
+            kstep(acc, g, 0, fa0, fb0, fa1, fb1);
+            kstep(acc, g, 1, fa1, fb1, fa0, fb0);
         }
         epilogue(j, acc);
     }
@@ -507,7 +497,8 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
                              hipStream_t stream) {
     auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL>;
-    // 136 KB of dynamic LDS is above the default launch limit; raise it once.
+    constexpr int LDS_BYTES = Ring<MX, KTAIL>::LDS;
+    // up to 160 KB of dynamic LDS is above the default launch limit; raise it once.
     static std::once_flag once;
     static hipError_t attr_status = hipSuccess;
     std::call_once(once, [&] {
@@ -531,8 +522,9 @@ template <bool MX>
 static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                               const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
                               int out_f32, hipStream_t stream) {
-    // mode (a) needs whole 64-byte stages; mode (b) also needs whole 4-byte scale dwords per stage pair
-    const bool tail = MX ? (k % (2 * BK)) != 0 : (k % BK) != 0;
+    // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
+    // past K and, in mode (b), reads the scales byte by byte from global memory
+    const bool tail = (k % BK) != 0;
     if (out_f32)
         return tail ? launch_one<MX, true, true>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
                     : launch_one<MX, true, false>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
@@ -540,10 +532,11 @@ static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A,
                 : launch_one<MX, false, false>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
 }
 
-// 32-bit buffer offsets: a 256-row panel of K bytes must stay below 2^32.
+// 32-bit buffer offsets: a 256-row panel of K bytes stays below 2^31, so the
+// out-of-range offset 2^31 plus any scalar offset still fits in 32 bits.
 static bool fits(int64_t m, int64_t n, int64_t k) {
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    return m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 24) && tiles < (1LL << 31);
+    return m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 23) && tiles < (1LL << 31);
 }
 
 hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
