@@ -64,6 +64,7 @@
 // the accumulators and the epilogue, under uniform control flow.
 
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -73,6 +74,7 @@ namespace fp8g {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256;        // tile rows (m)
 constexpr int BN = 256;        // tile cols (n)
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: kept in scalar registers
     const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, lhi = lane >> 5;
 
@@ -336,9 +338,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     snv[i][gq][t] = 1.0f;
-                    // dword loads (the backend merges them): extracting the elements of
-                    // a 128-bit buffer-load builtin one by one is folded to element 0
-                    // by this compiler at -O3
                     if constexpr (!MX) {
                         const int n = n0 + wn * WT + i * 32 + 8 * gq + 4 * lhi + t;
                         snv[i][gq][t] = __builtin_bit_cast(
@@ -391,6 +390,104 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         }
     };
 
+    // ---- bf16 epilogue through LDS (N % 8 == 0), in a free 32 KB region at
+    // stage_off: the tile's sa, sb sit at stage_off + 16 KB / + 17 KB (loaded by
+    // tile_scales_to_lds); each wave stages bands of 32 rows x 64 columns (4 KB,
+    // one 128-byte line per row) in its own 4 KB, reads them back row-contiguous
+    // and stores 16 bytes per lane, 8 rows x 128 bytes (whole lines) per
+    // instruction.  A store instruction that touches 32 rows at 16 bytes each
+    // runs about 8x slower.  Band layout: 32 rows of 128 bytes, logical 16-byte
+    // chunk c of row r in physical chunk c ^ ((r >> 1) & 7), its 8-byte halves
+    // swapped when r >= 16: the 8-byte writes of 32 rows and the 16-byte reads of
+    // 2 rows per LDS cycle both hit distinct banks.
+    constexpr uint32_t SC_OFF = 16384;   // sa at +16 KB, sb at +17 KB
+    auto tile_scales_to_lds = [&](int j, uint32_t stage_off) __attribute__((always_inline)) {
+        if constexpr (!MX) {
+            const TileCoord tc = tile_of(j);
+            const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+            const uint32_t v = (uint32_t)(64 * wave + lane) * 4u;   // lane L of wave w: element 64w + L
+            dma4(uniform(lds0 + stage_off + SC_OFF + (uint32_t)(wave * 256)), v,
+                 panel(sa + m0, (uint32_t)min(BM, M - m0) * 4u), 0u);
+            dma4(uniform(lds0 + stage_off + SC_OFF + 1024u + (uint32_t)(wave * 256)), v,
+                 panel(sb + n0, (uint32_t)min(BN, N - n0) * 4u), 0u);
+        }
+    };
+    auto epilogue_staged = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+        const TileCoord tc = tile_of(j);
+        const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+        const uint32_t rows = (uint32_t)min(BM, M - m0);
+        const __amdgpu_buffer_rsrc_t rsD =
+            panel(reinterpret_cast<uint8_t*>(Dv) + (int64_t)m0 * N * 2, rows * (uint32_t)N * 2u);
+        constexpr uint32_t OOB = 0x80000000u;
+        // lane-derived values are computed here from an opaque copy of the lane
+        // index: hoisted to the kernel start they would stay live through the
+        // main loop and be spilled, and each reload would wait for the stores
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        const int l32e = lane_e & 31, lhie = lane_e >> 5;
+        uint8_t* st = smem + stage_off + wave * 4096;
+        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
+        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
+        const uint32_t wkey = (uint32_t)((l32e >> 1) & 7), whalf = (uint32_t)(lhie ^ (l32e >> 4));
+        // rows past M need no check: the descriptor covers exactly the tile's rows
+        // of D, and offsets past it are dropped
+        const uint32_t rc = (uint32_t)(lane_e & 7);        // read-back: 16-byte chunk of the lane
+        const int rr = lane_e >> 3;                          // read-back: row within 8
+        const uint32_t rd_off = (uint32_t)(rr * 128) + ((rc ^ (uint32_t)((rr >> 1) & 3)) << 4);
+#pragma unroll
+        for (int ih = 0; ih < 2; ++ih) {          // column half of the wave tile: blocks i = 2ih, 2ih+1
+            float snv[2][4][4];
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    if constexpr (!MX) {
+                        // a float vector: __builtin_bit_cast of an element of an integer
+                        // vector reads element 0 whatever the index (clang)
+                        const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + (2 * ih + ii) * 32 + 8 * gq + 4 * lhie);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) snv[ii][gq][t] = t4[t];
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) snv[ii][gq][t] = 1.0f;
+                    }
+                }
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                float smv = 1.0f;
+                if constexpr (!MX) smv = lsa[wm * WT + jb * 32 + l32e];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = acc[2 * ih + ii][jb][4 * gq + t] * smv * snv[ii][gq][t];
+                        typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+                        const v2u w2 = {bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
+                        const uint32_t pc = (uint32_t)(4 * ii + gq) ^ wkey;
+                        *reinterpret_cast<v2u*>(st + l32e * 128 + pc * 16 + whalf * 8) = w2;
+                    }
+                const int n = n0 + wn * WT + 64 * ih + 8 * (int)rc;
+                // branch-free select (a compare-and-select here becomes a branch)
+                uint32_t keep = n < N ? 0xFFFFFFFFu : 0u;
+                asm volatile("" : "+v"(keep));
+                const uint32_t col_off = (uint32_t)n * 2u;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // band row r = 8k + rr: (r >> 1) & 7 = 4k + (rr >> 1) (mod 8), so the
+                    // physical chunk is rc ^ ((rr >> 1) & 3) ^ 4 (k & 1)
+                    v4u d = *reinterpret_cast<const v4u*>(st + k * 1024 + (rd_off ^ (uint32_t)(64 * (k & 1))));
+                    if (k >= 2) d = (v4u){d.z, d.w, d.x, d.y};   // rows 16..31: halves swapped
+                    const uint32_t mr = (uint32_t)(wm * WT + jb * 32 + 8 * k + rr);   // row inside the tile
+                    const uint32_t off = mr * (uint32_t)N * 2u + col_off;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, 0);
+                }
+            }
+        }
+    };
+    const bool staged = !OUT_F32 && (N % 8) == 0;
+
     if (nk == 0) {   // K == 0: every tile is the empty sum
         for (int j = 0; j < my_tiles; ++j) {
             v16f acc[NB][NB];
@@ -398,7 +495,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             for (int i = 0; i < NB; ++i)
 #pragma unroll
                 for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-            epilogue(j, acc);
+            if (staged) {
+                tile_scales_to_lds(j, 0);
+                wait_vmcnt<0>();
+                __syncthreads();
+                epilogue_staged(j, acc, 0);
+                __syncthreads();
+            } else {
+                epilogue(j, acc);
+            }
         }
         return;
     }
@@ -438,14 +543,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   16-byte LDS reads of the next step's fragments into the other register
     //   set.  Spreading the loads keeps the address unit from blocking the
     //   matrix-core steps behind a burst of loads from all four waves.
-    auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, const v8i* fa, const v8i* fb, v8i* na,
+    //   LAST (the tile's last step): no reads of the next step's fragments (they
+    //   are read after the epilogue, which then has their registers to itself).
+    auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
                      v8i* nbf) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last_tag)::value;
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<(NSLOT - 4) * LI>();
             __syncthreads();
+            // last stage of a tile: the slot of its B item is now free until the
+            // next tile's first step; load the tile's scales into it for the
+            // staged epilogue (before this step's item loads, so that waiting for
+            // all but those leaves the scales landed)
+            if constexpr (!MX && LAST) {
+                if (staged) tile_scales_to_lds(g / nk, (uint32_t)(slot_add(rslot, 1) * SLOT));
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         const int gn = h ? g + 1 : g, hn = h ^ 1;
@@ -458,10 +573,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
             if (k < LI) dma_item(k);
             // reads in order of first use: row block 0 of B, the four of A, then B 1..3
-            if (k == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
-            if (k >= 1 && k <= 4) na[k - 1] = frag(sa_off, frag_a, hn, k - 1);
-            if (k >= 5 && k <= 7) nbf[k - 4] = frag(sb_off, frag_b, hn, k - 4);
-            if (k == 9) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+            if constexpr (!LAST) {
+                if (k == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
+                if (k >= 1 && k <= 4) na[k - 1] = frag(sa_off, frag_a, hn, k - 1);
+                if (k >= 5 && k <= 7) nbf[k - 4] = frag(sb_off, frag_b, hn, k - 4);
+                if (k == 9) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         advance();
@@ -469,12 +586,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         // keep this step's operand registers allocated to its end
 #pragma unroll
         for (int i = 0; i < NB; ++i) asm volatile("" : : "v"(fa[i]), "v"(fb[i]));
+        if constexpr (!LAST) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            xa[i] = nxa[i];
-            xb[i] = nxb[i];
+            for (int i = 0; i < NB; ++i) {
+                xa[i] = nxa[i];
+                xb[i] = nxb[i];
+            }
         }
     };
+    using NotLast = std::integral_constant<bool, false>;
+    using Last = std::integral_constant<bool, true>;
 
     int g = 0;
     for (int j = 0; j < my_tiles; ++j) {
@@ -483,11 +604,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-        for (int s = 0; s < nk; ++s, ++g) {
-            kstep(acc, g, 0, fa0, fb0, fa1, fb1);
-            kstep(acc, g, 1, fa1, fb1, fa0, fb0);
+        for (int s = 0; s < nk - 1; ++s, ++g) {
+            kstep(acc, g, 0, NotLast{}, fa0, fb0, fa1, fb1);
+            kstep(acc, g, 1, NotLast{}, fa1, fb1, fa0, fb0);
         }
-        epilogue(j, acc);
+        kstep(acc, g, 0, NotLast{}, fa0, fb0, fa1, fb1);
+        kstep(acc, g, 1, Last{}, fa1, fb1, fa0, fb0);
+        ++g;
+        if (staged) {
+            // the slot of the last stage's B item is free until the next K step
+            // loads into it (every wave finished reading it before the last barrier)
+            if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
+            __syncthreads();
+            epilogue_staged(j, acc, (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
+            __syncthreads();   // staging reads done before that slot is loaded again
+        } else {
+            epilogue(j, acc);
+        }
+        // the next stage's step-0 fragments and scales (its items landed before
+        // the last barrier; the slots of this stage's items are not refilled
+        // before the next barrier)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            fa0[i] = frag((uint32_t)(rslot * SLOT), frag_a, 0, i);
+            fb0[i] = frag((uint32_t)(slot_add(rslot, 1) * SLOT), frag_b, 0, i);
+        }
+        read_scales(g, 0, (uint32_t)(rslot * SLOT), (uint32_t)(slot_add(rslot, 1) * SLOT), xa, xb);
     }
     wait_vmcnt<0>();   // the past-the-end loads must land before the workgroup exits
 }
