@@ -29,10 +29,12 @@ def check_rows(fp8g, x, what):
                              % (what, int((q != qr).sum()), r, c, x[r, c], q[r, c], qr[r, c]))
 
 
-# shapes exercise every kernel variant: vector rows of 1..32 float4 per lane,
-# the two-pass vector path (> 8192 per row), and the element-wise path (cols % 4 != 0)
+# shapes exercise every kernel variant: one wave per row (up to 1024 columns),
+# one workgroup per row with the row in registers (up to 16384), the two-pass
+# workgroup path (longer rows), and the element-wise path (cols % 4 != 0)
 SHAPES = [(1, 4), (3, 16), (5, 60), (7, 256), (9, 260), (128, 512), (6, 1000), (4, 2048), (33, 4096),
-          (130, 8192), (3, 8196), (4, 10000), (5, 257), (9, 1002), (2, 1), (3, 3), (64, 4099)]
+          (130, 8192), (3, 8196), (4, 10000), (5, 257), (9, 1002), (2, 1), (3, 3), (64, 4099),
+          (3, 16384), (5, 16388), (2, 40000)]
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)
@@ -118,6 +120,36 @@ def test_cast_every_fp32_pattern_up_to_448(gpu_lib):
                                      % (int(bits[i]), int(sign), int(qc[:, 4:].reshape(-1)[i]),
                                         int(exp.reshape(-1)[i])))
         start += n
+
+
+def test_quantize_division_near_rounding_boundaries(gpu_lib):
+    """Quotients x / s within 3 fp32 ulps of every E4M3 rounding boundary (both
+    signs), for 2048 row scales log-uniform in [2^-20, 2^20], scales whose
+    significand is all ones or exactly 1, and scales below the smallest normal
+    fp32.  The codes match the oracle only if the kernel's quotient is the
+    correctly rounded fp32 division x / s for every one of them."""
+    thr = np.array(_thresholds(), dtype=np.uint32).view(np.float32).astype(np.float64)   # 126 boundaries
+    u = synth.uniform(synth.stream_key(0x5EED, 1), 0, 2048)
+    s0 = np.concatenate([np.exp2(40.0 * u - 20.0),
+                         np.ldexp(2.0 - 2.0 ** -23, np.arange(-20, 20)),       # significand all ones
+                         np.ldexp(1.0, np.arange(-20, 20)),                    # powers of two
+                         np.ldexp(1.0 + u[:16], -130)])                        # subnormal scales
+    amax = (448.0 * s0).astype(np.float32)
+    s = amax / np.float32(448.0)                                               # the scale each row gets
+    cols = 1792
+    x = np.zeros((len(s0), cols), np.float32)
+    x[:, 0] = amax
+    base = (thr[None, :] * s.astype(np.float64)[:, None]).astype(np.float32)   # RN(m s)
+    c = 1
+    for k in range(-3, 4):
+        v = base.copy()
+        for _ in range(abs(k)):
+            v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(0.0))
+        for sign in (1.0, -1.0):
+            x[:, c:c + thr.size] = np.float32(sign) * v
+            c += thr.size
+    assert c <= cols
+    check_rows(gpu_lib, x, "division near rounding boundaries")
 
 
 @pytest.mark.parametrize("side,rows", [("a", None), ("b", slice(0, 4096))])
