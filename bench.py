@@ -8,8 +8,10 @@ input already resident in HBM:
       fp8_quantize_rowwise(X_A) -> A, sa      (activations, per token)
       fp8_quantize_rowwise(X_B) -> B, sb      (weights, per output channel)
       fp8_gemm_scaled(A, B, sa, sb) -> D      (bf16)
-  mx (4096 x 14336 x 4096, MXFP8): mxfp8_gemm on E4M3 codes + UE8M0 scales
-      produced by the MX quantizer kernel from the fp32 operands.
+  mx (4096 x 14336 x 4096, MXFP8):
+      mxfp8_quantize(X_A) -> A, ea            (UE8M0 per 32 K elements)
+      mxfp8_quantize(X_B) -> B, eb
+      mxfp8_gemm(A, B, ea, eb) -> D           (bf16)
 `value` = 2 M N K / (mean step time), in TFLOP/s.  Prints one JSON line.
 
 The line also carries
@@ -200,7 +202,24 @@ def main():
                 ev[3].record(stream)
         kernels = ["quantize_activations", "quantize_weights", "gemm"]
     else:
-        raise SystemExit("mx workload needs the GPU MX quantizer")
+        qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        qb = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        ea = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        eb = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+
+        def step(ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            fp8g.mxfp8_quantize(XA, qa, ea)
+            if ev is not None:
+                ev[1].record(stream)
+            fp8g.mxfp8_quantize(XB, qb, eb)
+            if ev is not None:
+                ev[2].record(stream)
+            fp8g.mxfp8_gemm(M, N, K, qa, qb, ea, eb, D=D)
+            if ev is not None:
+                ev[3].record(stream)
+        kernels = ["quantize_activations", "quantize_weights", "gemm"]
 
     log("warmup", args.warmup)
     for _ in range(args.warmup):
@@ -248,7 +267,9 @@ def main():
     }
     if w.mode == "a":
         qbytes = {"quantize_activations": M * K * 5 + 4 * M, "quantize_weights": N * K * 5 + 4 * N}
-        line["quantizer_gbs"] = {k: round(b / (per_kernel[k] * 1e-6) / 1e9, 1) for k, b in qbytes.items()}
+    else:   # codes + one scale byte per 32 elements
+        qbytes = {"quantize_activations": M * K * 5 + M * K // 32, "quantize_weights": N * K * 5 + N * K // 32}
+    line["quantizer_gbs"] = {k: round(b / (per_kernel[k] * 1e-6) / 1e9, 1) for k, b in qbytes.items()}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline_ffn_up(w) if w.mode == "a" else cpu_baseline_mx(w)

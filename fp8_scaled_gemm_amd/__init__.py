@@ -9,6 +9,7 @@ There is no fallback: if the library is missing, every call raises.
 Functions keep the C names and argument order:
 
     fp8_quantize_rowwise(x)                              -> (q, scale)
+    mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
 
@@ -20,7 +21,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["load", "fp8_quantize_rowwise", "fp8_gemm_scaled", "mxfp8_gemm", "status_string",
+__all__ = ["load", "fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "status_string",
            "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +35,7 @@ _VOIDP = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _SIGNATURES = {
     "fp8_quantize_rowwise": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
+    "mxfp8_quantize": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
 }
@@ -144,6 +146,30 @@ def fp8_quantize_rowwise(x, q=None, scale=None):
     _need(scale, "scale", torch.float32, (R,))
     _check(load().fp8_quantize_rowwise(_ptr(x), R, C, _ptr(qc), _ptr(scale), _stream()),
            "fp8_quantize_rowwise")
+    return q, scale
+
+
+def mxfp8_quantize(x, q=None, scale=None):
+    """MXFP8 block quantization of a 2-D fp32 device tensor (cols % 32 == 0).
+
+    Returns (q: float8_e4m3fn [R, C], scale: uint8 UE8M0 codes [R, C/32]) with
+    x ~ q * 2^(scale - 127) per block of 32 along a row.
+    """
+    torch = _torch()
+    _need(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if C % 32:
+        raise ValueError("the row length must be a multiple of 32 for MXFP8")
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    qc = _as_codes(q, "q")
+    _need(qc, "q", shape=(R, C))
+    _need(scale, "scale", torch.uint8, (R, C // 32))
+    _check(load().mxfp8_quantize(_ptr(x), R, C, _ptr(qc), _ptr(scale), _stream()), "mxfp8_quantize")
     return q, scale
 
 

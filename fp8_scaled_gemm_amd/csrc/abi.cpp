@@ -75,6 +75,18 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q,
     return hip_status(fp8g::launch_quantize_rowwise(x, rows, cols, q, scale, stream));
 }
 
+int mxfp8_quantize(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || cols % 32 != 0) return FP8G_ERR_SHAPE;
+    const int64_t n = mul3(rows, cols, 1);
+    if (n < 0 || n > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (n == 0) return FP8G_OK;
+    if (!x || !q || !scale) return FP8G_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return FP8G_ERR_ALIGN;
+    const Range rx = range_of(x, n * 4), rq = range_of(q, n), rs = range_of(scale, n / 32);
+    if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return FP8G_ERR_OVERLAP;
+    return hip_status(fp8g::launch_quantize_mx(x, rows, cols, q, scale, stream));
+}
+
 int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* scale_a,
                     const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
     const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * 4, n * 4, D, out_dtype);
@@ -96,7 +108,7 @@ const char* fp8g_status_string(int status) {
     switch (status) {
         case FP8G_OK: return "ok";
         case FP8G_ERR_NULL: return "a required pointer is NULL";
-        case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k not a multiple of 32 for MXFP8)";
+        case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k / cols not a multiple of 32 for MXFP8)";
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case FP8G_ERR_DTYPE: return "unknown output dtype";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";

@@ -5,6 +5,8 @@
  *
  * Operations (definitions in each entry point's comment):
  *   fp8_quantize_rowwise  fp32 [rows, cols] -> E4M3 codes + one fp32 scale per row
+ *   mxfp8_quantize        fp32 [rows, cols] -> E4M3 codes + one UE8M0 scale per
+ *                         32 consecutive elements of a row (MXFP8)
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
  *   mxfp8_gemm            same product with one power-of-two scale per 32 K
  *                         elements of every row of A and of B (MXFP8)
@@ -104,6 +106,34 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
                     const uint8_t* A, const uint8_t* B,
                     const float* scale_a, const float* scale_b,
                     void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * mxfp8_quantize -- MXFP8 block quantization (the step before mxfp8_gemm).
+ *
+ * Source: the page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm 통합", section 1:
+ * one unsigned-byte scale per 32 elements along K, the scale tensor shaped
+ * (rows, cols // 32).  The byte is UE8M0: code c stands for 2^(c - 127).  For
+ * block j of row r (elements 32j .. 32j+31):
+ *
+ *   amax   = max |x[r, 32j + t]|
+ *   e      = the smallest integer with amax <= 448 * 2^e, clamped to
+ *            [-127, 127]; e = -127 for an all-zero block
+ *   scale[r, j] = e + 127
+ *   q[r, 32j + t] = E4M3_RNE(x[r, 32j + t] * 2^-e)   (exact power-of-two
+ *            scaling; never above 448, so the cast never saturates; the sign
+ *            of zero is kept)
+ * so that x ~ decode(q) * 2^(scale - 127).
+ *
+ * x      device, fp32 [rows, cols], read only
+ * q      device, E4M3 codes [rows, cols], written
+ * scale  device, UE8M0 codes [rows, cols / 32], written
+ * cols % 32 != 0 -> ERR_SHAPE.  rows == 0 or cols == 0: no-op.
+ * NaN/Inf in x are outside the contract.  Bit-exact with the definition.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_OVERLAP, ERR_UNSUPPORTED
+ * (size overflow), ERR_HIP.
+ */
+int mxfp8_quantize(const float* x, int64_t rows, int64_t cols,
+                   uint8_t* q, uint8_t* scale, hipStream_t stream);
 
 /*
  * mxfp8_gemm -- MXFP8 block-scaled GEMM.

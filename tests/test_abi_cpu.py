@@ -27,7 +27,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
-    assert set(names) == {"fp8_quantize_rowwise", "fp8_gemm_scaled", "mxfp8_gemm", "fp8g_status_string"}
+    assert set(names) == {"fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
+                          "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -105,6 +106,29 @@ def test_quantize_argument_checks(lib):
     assert quant(lib, q=P_(64)) == OVERLAP                    # q inside x
     assert quant(lib, s=P_((1 << 30) + 16)) == OVERLAP        # scale inside q
     assert quant(lib, cols=0, x=None, q=None) in (OK, HIP)    # empty rows: only scales written
+
+
+def mxq(lib, x=P_(0), rows=8, cols=64, q=P_(1 << 30), s=P_(2 << 30)):
+    return lib.mxfp8_quantize(x, rows, cols, q, s, ctypes.c_void_p(S))
+
+
+def test_mx_quantize_argument_checks(lib):
+    assert mxq(lib, rows=-1) == SHAPE
+    assert mxq(lib, cols=-32) == SHAPE
+    for cols in (16, 33, 48, 1):                              # blocks of 32 along a row
+        assert mxq(lib, cols=cols) == SHAPE
+    assert mxq(lib, rows=0, x=None, q=None, s=None) == OK      # empty: no-op
+    assert mxq(lib, cols=0, x=None, q=None, s=None) == OK
+    assert mxq(lib, x=None) == NULL
+    assert mxq(lib, q=None) == NULL
+    assert mxq(lib, s=None) == NULL
+    assert mxq(lib, x=P_(4)) == ALIGN
+    assert mxq(lib, q=P_((1 << 30) + 8)) == ALIGN
+    assert mxq(lib, s=P_((2 << 30) + 1)) == ALIGN
+    assert mxq(lib, q=P_(1024)) == OVERLAP                     # q inside x (8 x 64 fp32 = 2 KB)
+    assert mxq(lib, s=P_((1 << 30) + 256)) == OVERLAP          # scales inside q (512 B)
+    assert mxq(lib, s=P_((1 << 30) + 512)) in (OK, HIP)        # adjacent: proceeds to the launch
+    assert mxq(lib, rows=1 << 40, cols=1 << 30) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
