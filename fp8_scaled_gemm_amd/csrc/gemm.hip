@@ -99,8 +99,18 @@ struct Ring {
     static constexpr int SLOT = OP_BYTES + (SCALES ? SCALE_BYTES : 0);
     static constexpr int LDS = NSLOT * SLOT;
     static constexpr int LOADS = DMA_PER_ITEM + (SCALES ? 1 : 0);   // load instructions per item and wave
+    // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
+    // slots are free (its step 1), so both its items are issued in that step
+    // (none in step 0) to give them the longest lead.  5 slots: one item per
+    // step, four items ahead.
+    static constexpr bool PAIRED = NSLOT == 4;
+    // bf16 epilogue staging (16 KB): 5 slots borrow the slot that is free
+    // during the epilogue; 4 (paired) slots have none free, so a region after
+    // the ring is used
+    static constexpr int STAGE_AREA = LDS;
+    static constexpr int LDS_TOTAL = LDS + (PAIRED ? 16 * 1024 : 0);
 };
-static_assert(Ring<false, false>::LDS <= 160 * 1024 && Ring<true, false>::LDS <= 160 * 1024, "LDS");
+static_assert(Ring<false, false>::LDS_TOTAL <= 160 * 1024 && Ring<true, false>::LDS_TOTAL <= 160 * 1024, "LDS");
 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
 
@@ -512,12 +522,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // ---- prologue: items 0 .. NSLOT-2 in flight; stage 0 (items 0, 1) landed
     // and the fragments of its step 0 read
     cursor_tile();
-    for (int i = 0; i < NSLOT - 1; ++i) {
+    constexpr int PRO_ITEMS = R::PAIRED ? 4 : NSLOT - 1;   // items in flight before step 0
+    for (int i = 0; i < PRO_ITEMS; ++i) {
 #pragma unroll
         for (int q = 0; q < LI; ++q) dma_item(q);
         advance();
     }
-    wait_vmcnt<(NSLOT - 3) * LI>();
+    wait_vmcnt<(PRO_ITEMS - 2) * LI>();
     __syncthreads();
 
     // Fragment registers are double-buffered: step t computes from one set
@@ -552,7 +563,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<(NSLOT - 4) * LI>();
+            // stage g+1's items landed: with 5 slots one later item may be in
+            // flight; with 4 (paired) none
+            wait_vmcnt<(R::PAIRED ? 0 : NSLOT - 4) * LI>();
             __syncthreads();
             // last stage of a tile: the slot of its B item is now free until the
             // next tile's first step; load the tile's scales into it for the
@@ -571,7 +584,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int k = 0; k < 12; ++k) {
             const int i = 1 + k / 4, jb = k % 4;
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
-            if (k < LI) dma_item(k);
+            if constexpr (!R::PAIRED) {
+                if (k < LI) dma_item(k);
+            } else if (h == 1) {
+                // the stage's two items: the first over slots 0-5, the second over 6-11
+                const int kk = k % 6;
+#pragma unroll
+                for (int q = kk * LI / 6; q < (kk + 1) * LI / 6; ++q) dma_item(q);
+                if (k == 5) advance();
+            }
             // reads in order of first use: row block 0 of B, the four of A, then B 1..3
             if constexpr (!LAST) {
                 if (k == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
@@ -581,7 +602,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        advance();
+        if (!R::PAIRED || h == 1) advance();
         if (h) rslot = na_slot;
         // keep this step's operand registers allocated to its end
 #pragma unroll
@@ -616,7 +637,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             // loads into it (every wave finished reading it before the last barrier)
             if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
-            epilogue_staged(j, acc, (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
+            epilogue_staged(j, acc, R::PAIRED ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
             __syncthreads();   // staging reads done before that slot is loaded again
         } else {
             epilogue(j, acc);
@@ -639,7 +660,7 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
                              hipStream_t stream) {
     auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL>;
-    constexpr int LDS_BYTES = Ring<MX, KTAIL>::LDS;
+    constexpr int LDS_BYTES = Ring<MX, KTAIL>::LDS_TOTAL;
     // up to 160 KB of dynamic LDS is above the default launch limit; raise it once.
     static std::once_flag once;
     static hipError_t attr_status = hipSuccess;
