@@ -38,7 +38,9 @@ import synth  # noqa: E402
 
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = {"ffn_up": "c4_ffn_up_8192x22016x8192", "mx": "c5_mx_4096x14336x4096"}
+WORKLOADS = {"ffn_up": "c4_ffn_up_8192x22016x8192", "mx": "c5_mx_4096x14336x4096",
+             "concat_mla": "concat_mla_k_fp8_16384x128"}
+CONCAT_T, CONCAT_H = 16384, 128     # tokens x heads, 1-byte elements, rope shared by a token's heads
 
 
 def log(*a):
@@ -50,7 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up")
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up",
+                   help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic", default=None,
                    help="counter summary with the measured HBM bytes per GEMM launch (default: the one "
@@ -157,6 +160,59 @@ def _blas_threads():
     return os.cpu_count() or 1
 
 
+def concat_bench(args, torch, fp8g):
+    """concat_mla_k on FP8 (1-byte) elements: k [T, H, 192] from k_nope [T, H, 128]
+    and a rope part [T, 1, 64] shared by each token's heads.  value = algorithmic
+    bytes (k_nope + k_rope read, k written) per second."""
+    T, H = CONCAT_T, CONCAT_H
+    dev = torch.device("cuda", 0)
+    bits = synth.raw_u64(synth.stream_key(0xC0C0A7, 1), 0, T * H * 128 // 8)
+    nope = torch.from_numpy(bits.view(np.uint8).reshape(T, H, 128)).to(dev).view(torch.float8_e4m3fn)
+    bits = synth.raw_u64(synth.stream_key(0xC0C0A7, 2), 0, T * 64 // 8)
+    rope = torch.from_numpy(bits.view(np.uint8).reshape(T, 1, 64)).to(dev).view(torch.float8_e4m3fn)
+    k = torch.empty((T, H, 192), dtype=torch.float8_e4m3fn, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fp8g.concat_mla_k(nope, rope, k)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fp8g.concat_mla_k(nope, rope, k)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = T * H * 128 + T * 64 + T * H * 192
+    ms = elapsed / args.steps * 1e3
+    line = {"metric": "concat_mla_k GB/s (FP8, %d tokens x %d heads, rope shared)" % (T, H),
+            "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": WORKLOADS["concat_mla"], "tokens": T, "heads": H, "nope": 128, "rope": 64,
+                       "elem_bytes": 1, "rope_heads": 1},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "kernel": "concat_mla_k_kernel", "bytes_per_launch": nbytes}}
+    if not args.no_cpu_baseline:
+        from oracle import concat
+        ts = 2048                                            # tokens in the sample
+        n = nope[:ts].view(torch.uint8).cpu().numpy()
+        r = rope[:ts].view(torch.uint8).cpu().numpy()
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < 10.0:
+            concat.concat_mla_k(n, r)
+            reps += 1
+        dt = (time.perf_counter() - t1) / reps
+        line["cpu_baseline"] = {"value": round(ts * (H * 320 + 64) / dt / 1e9, 2), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "seconds": round(dt * reps, 2),
+                                "sample": "oracle concat_mla_k (numpy) on the first %d tokens, repeated %d times"
+                                          % (ts, reps)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,6 +228,9 @@ def main():
         copy_only(args.copy_bytes)
         return
     fp8g.load()
+    if args.workload == "concat_mla":
+        concat_bench(args, torch, fp8g)
+        return
     w = synth.WORKLOADS[WORKLOADS[args.workload]]
     dev = torch.device("cuda", 0)
 

@@ -12,6 +12,7 @@ Functions keep the C names and argument order:
     mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
+    concat_mla_k(k_nope, k_rope)                         -> k  (MLA key rows)
 
 E4M3 tensors are ``torch.float8_e4m3fn`` (OCP, the gfx950 format) or raw
 ``torch.uint8`` codes; the FNUZ variant of gfx942 is rejected.
@@ -21,7 +22,8 @@ import ctypes
 import os
 import re
 
-__all__ = ["load", "fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "status_string",
+__all__ = ["load", "fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "concat_mla_k",
+           "status_string",
            "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +40,7 @@ _SIGNATURES = {
     "mxfp8_quantize": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
+    "concat_mla_k": [_VOIDP, _VOIDP, _VOIDP, _I64, _I64, _I64, ctypes.c_int, _VOIDP],
 }
 
 
@@ -215,3 +218,29 @@ def mxfp8_gemm(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
     _check(load().mxfp8_gemm(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D), code,
                              _stream()), "mxfp8_gemm")
     return D
+
+
+def concat_mla_k(k_nope, k_rope, k=None):
+    """MLA key rows: k [T, H, 192] = k_nope [T, H, 128] ++ k_rope [T, R, 64],
+    R = 1 (shared by a token's heads) or H.  1-byte (float8_e4m3fn,
+    float8_e5m2, uint8) or 2-byte (bfloat16, float16, int16/uint16) elements,
+    copied bit for bit."""
+    torch = _torch()
+    if k_nope.dim() != 3 or k_nope.shape[2] != 128:
+        raise ValueError("k_nope must be [T, H, 128]")
+    T, H, _ = k_nope.shape
+    if k_rope.dim() != 3 or k_rope.shape[0] != T or k_rope.shape[2] != 64 or k_rope.shape[1] not in (1, H):
+        raise ValueError("k_rope must be [T, 1, 64] or [T, H, 64]")
+    if k_rope.dtype != k_nope.dtype:
+        raise TypeError("k_nope and k_rope must have the same dtype")
+    esz = k_nope.element_size()
+    if esz not in (1, 2):
+        raise TypeError("elements must be 1 or 2 bytes, got %s" % k_nope.dtype)
+    _need(k_nope, "k_nope")
+    _need(k_rope, "k_rope")
+    if k is None:
+        k = torch.empty((T, H, 192), dtype=k_nope.dtype, device=k_nope.device)
+    _need(k, "k", k_nope.dtype, (T, H, 192))
+    _check(load().concat_mla_k(_ptr(k), _ptr(k_nope), _ptr(k_rope), T, H, k_rope.shape[1], esz, _stream()),
+           "concat_mla_k")
+    return k

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8g.so")
-SOURCES = ["abi.cpp", "quantize.hip", "mx_quantize.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "mx_quantize.hip", "concat.hip", "gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -104,13 +104,30 @@ int mxfp8_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t*
     return hip_status(fp8g::launch_gemm_mx(m, n, k, A, B, scale_a, scale_b, D, out_dtype == FP8G_OUT_F32, stream));
 }
 
+int concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens, int64_t heads,
+                 int64_t rope_heads, int elem_bytes, hipStream_t stream) {
+    if (tokens < 0 || heads < 0) return FP8G_ERR_SHAPE;
+    if (elem_bytes != 1 && elem_bytes != 2) return FP8G_ERR_DTYPE;
+    if (tokens == 0 || heads == 0) return FP8G_OK;
+    if (rope_heads != 1 && rope_heads != heads) return FP8G_ERR_SHAPE;
+    const int64_t k_bytes = mul3(tokens, heads, 192 * elem_bytes);
+    const int64_t n_bytes = mul3(tokens, heads, 128 * elem_bytes);
+    const int64_t r_bytes = mul3(tokens, rope_heads, 64 * elem_bytes);
+    if (k_bytes < 0 || n_bytes < 0 || r_bytes < 0 || k_bytes > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (!k || !k_nope || !k_rope) return FP8G_ERR_NULL;
+    if (!aligned16(k) || !aligned16(k_nope) || !aligned16(k_rope)) return FP8G_ERR_ALIGN;
+    const Range rk = range_of(k, k_bytes);
+    if (overlaps(rk, range_of(k_nope, n_bytes)) || overlaps(rk, range_of(k_rope, r_bytes))) return FP8G_ERR_OVERLAP;
+    return hip_status(fp8g::launch_concat_mla_k(k, k_nope, k_rope, tokens, heads, rope_heads, elem_bytes, stream));
+}
+
 const char* fp8g_status_string(int status) {
     switch (status) {
         case FP8G_OK: return "ok";
         case FP8G_ERR_NULL: return "a required pointer is NULL";
         case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k / cols not a multiple of 32 for MXFP8)";
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case FP8G_ERR_DTYPE: return "unknown output dtype";
+        case FP8G_ERR_DTYPE: return "unknown output dtype or element size";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
         case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (k % 16 for fp8_gemm_scaled, or size overflow)";
         case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";

@@ -13,6 +13,10 @@ hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t cols, u
 hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale,
                               hipStream_t stream);
 
+// MLA key rows: k [T, H, 192] = k_nope [T, H, 128] ++ k_rope [T, R, 64] (R = 1 or H)
+hipError_t launch_concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens, int64_t heads,
+                               int64_t rope_heads, int elem_bytes, hipStream_t stream);
+
 // mode (a): per-token x per-channel fp32 scales
 hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                               const float* sa, const float* sb, void* D, int out_f32, hipStream_t stream);

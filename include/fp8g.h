@@ -10,6 +10,8 @@
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
  *   mxfp8_gemm            same product with one power-of-two scale per 32 K
  *                         elements of every row of A and of B (MXFP8)
+ *   concat_mla_k          MLA key rows: 128 "nope" + 64 "rope" elements of
+ *                         1-byte (E4M3 / E5M2) or 2-byte type
  *
  * Common conventions
  *   - Every array is dense and row-major; the caller owns all memory.  A is
@@ -46,7 +48,7 @@ typedef enum {
     FP8G_ERR_NULL = 1,        /* required pointer is NULL */
     FP8G_ERR_SHAPE = 2,       /* negative extent, or k not a multiple of 32 for MXFP8 */
     FP8G_ERR_ALIGN = 3,       /* pointer not 16-byte aligned */
-    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype */
+    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype or element size */
     FP8G_ERR_OVERLAP = 5,     /* an output overlaps an input or another output */
     FP8G_ERR_UNSUPPORTED = 6, /* valid but outside this build's limits (see each call) */
     FP8G_ERR_HIP = 7          /* the HIP runtime refused the launch */
@@ -160,6 +162,30 @@ int mxfp8_gemm(int64_t m, int64_t n, int64_t k,
                const uint8_t* A, const uint8_t* B,
                const uint8_t* scale_a, const uint8_t* scale_b,
                void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * concat_mla_k -- assemble MLA key rows from their nope and rope parts.
+ *
+ * Source: the page on FlashInfer's concat_mla_k with FP8 (E4M3 / E5M2)
+ * inputs, sections 1-3: each key row is 128 nope elements followed by 64
+ * rope elements; elements of 1 byte (E4M3, E5M2) or 2 bytes (BF16, FP16) are
+ * moved unchanged (bit-exact).
+ *
+ *   k[t, h, 0:128]   = k_nope[t, h, 0:128]
+ *   k[t, h, 128:192] = k_rope[t, (rope_heads == 1 ? 0 : h), 0:64]
+ *
+ * k       device, [tokens, heads, 192] elements, written
+ * k_nope  device, [tokens, heads, 128] elements, read only
+ * k_rope  device, [tokens, rope_heads, 64] elements, read only; rope_heads is
+ *         1 (one rope part per token, shared by its heads) or heads
+ * elem_bytes  1 or 2 (else ERR_DTYPE); all arrays dense, row-major.
+ * tokens == 0 or heads == 0: no-op.  Errors: ERR_NULL, ERR_SHAPE (negative
+ * extent, rope_heads not 1 or heads), ERR_DTYPE, ERR_ALIGN, ERR_OVERLAP
+ * (k overlaps an input), ERR_UNSUPPORTED (size overflow), ERR_HIP.
+ */
+int concat_mla_k(void* k, const void* k_nope, const void* k_rope,
+                 int64_t tokens, int64_t heads, int64_t rope_heads,
+                 int elem_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8g_status_string(int status);

@@ -15,10 +15,12 @@ out in numpy/float64 so that a reader can check it against the pages by eye.
 * ``gemm``  -- the two GEMM definitions (per-token x per-channel scales, and
   MXFP8 block scales) accumulated in float64, their error bound, and the
   element-by-element parity check.
+* ``concat`` -- concat_mla_k, the MLA key assembly (128 nope + 64 rope
+  elements per row) on raw 1- or 2-byte elements.
 
 Pins: ``tests/test_oracle_*.py`` hold every check that ties these functions to
 something other than themselves (the format definition, torch's own E4M3 cast,
 exact rational arithmetic, closed forms, brute force).
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, concat  # noqa: F401

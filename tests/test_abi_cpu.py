@@ -28,7 +28,7 @@ def lib():
 def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
     assert set(names) == {"fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
-                          "fp8g_status_string"}
+                          "concat_mla_k", "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -129,6 +129,30 @@ def test_mx_quantize_argument_checks(lib):
     assert mxq(lib, s=P_((1 << 30) + 256)) == OVERLAP          # scales inside q (512 B)
     assert mxq(lib, s=P_((1 << 30) + 512)) in (OK, HIP)        # adjacent: proceeds to the launch
     assert mxq(lib, rows=1 << 40, cols=1 << 30) == UNSUPPORTED
+
+
+def cmk(lib, k=P_(2 << 30), nope=P_(0), rope=P_(1 << 30), T=4, H=8, R=1, e=1):
+    return lib.concat_mla_k(k, nope, rope, T, H, R, e, ctypes.c_void_p(S))
+
+
+def test_concat_mla_k_argument_checks(lib):
+    assert cmk(lib, T=-1) == SHAPE
+    assert cmk(lib, H=-1) == SHAPE
+    assert cmk(lib, e=3) == DTYPE
+    assert cmk(lib, e=4) == DTYPE
+    assert cmk(lib, T=0, k=None, nope=None, rope=None) == OK      # empty: no-op
+    assert cmk(lib, H=0, k=None, nope=None, rope=None) == OK
+    assert cmk(lib, R=2) == SHAPE                                   # rope heads: 1 or H
+    assert cmk(lib, R=8) in (OK, HIP)
+    assert cmk(lib, k=None) == NULL
+    assert cmk(lib, nope=None) == NULL
+    assert cmk(lib, rope=None) == NULL
+    assert cmk(lib, k=P_((2 << 30) + 8)) == ALIGN
+    assert cmk(lib, rope=P_((1 << 30) + 2)) == ALIGN
+    assert cmk(lib, k=P_(4 * 8 * 128 - 16)) == OVERLAP               # k starts inside k_nope
+    assert cmk(lib, k=P_(4 * 8 * 128)) in (OK, HIP)                  # adjacent
+    assert cmk(lib, k=P_((1 << 30) - 16)) == OVERLAP                 # k runs into k_rope
+    assert cmk(lib, T=1 << 40, H=1 << 20) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
