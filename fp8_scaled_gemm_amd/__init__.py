@@ -9,6 +9,7 @@ There is no fallback: if the library is missing, every call raises.
 Functions keep the C names and argument order:
 
     fp8_quantize_rowwise(x)                              -> (q, scale)
+    fp8_quantize_ex(x, per_tensor=False)                 -> (q, scale)  (fp32 or bf16 x)
     mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
@@ -22,7 +23,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["load", "fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "concat_mla_k",
+__all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "concat_mla_k",
            "status_string",
            "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32"]
 
@@ -38,6 +39,7 @@ _I64 = ctypes.c_int64
 _SIGNATURES = {
     "fp8_quantize_rowwise": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
     "mxfp8_quantize": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
+    "fp8_quantize_ex": [_VOIDP, ctypes.c_int, _I64, _I64, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "concat_mla_k": [_VOIDP, _VOIDP, _VOIDP, _I64, _I64, _I64, ctypes.c_int, _VOIDP],
@@ -149,6 +151,36 @@ def fp8_quantize_rowwise(x, q=None, scale=None):
     _need(scale, "scale", torch.float32, (R,))
     _check(load().fp8_quantize_rowwise(_ptr(x), R, C, _ptr(qc), _ptr(scale), _stream()),
            "fp8_quantize_rowwise")
+    return q, scale
+
+
+IN_F32, IN_BF16 = 0, 1
+SCALE_PER_ROW, SCALE_PER_TENSOR = 0, 1
+
+
+def fp8_quantize_ex(x, per_tensor=False, q=None, scale=None):
+    """E4M3 quantization of a 2-D fp32 or bf16 device tensor with scale
+    amax / 448, one per row (scale [R]) or one per tensor (scale [1])."""
+    torch = _torch()
+    if x.dtype == torch.float32:
+        code = IN_F32
+    elif x.dtype == torch.bfloat16:
+        code = IN_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+    _need(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty((1 if per_tensor else R,), dtype=torch.float32, device=x.device)
+    qc = _as_codes(q, "q")
+    _need(qc, "q", shape=(R, C))
+    _need(scale, "scale", torch.float32, (1 if per_tensor else R,))
+    _check(load().fp8_quantize_ex(_ptr(x), code, R, C, SCALE_PER_TENSOR if per_tensor else SCALE_PER_ROW,
+                                  _ptr(qc), _ptr(scale), _stream()), "fp8_quantize_ex")
     return q, scale
 
 

@@ -75,6 +75,24 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q,
     return hip_status(fp8g::launch_quantize_rowwise(x, rows, cols, q, scale, stream));
 }
 
+int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int granularity, uint8_t* q,
+                    float* scale, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
+    if (in_dtype != FP8G_IN_F32 && in_dtype != FP8G_IN_BF16) return FP8G_ERR_DTYPE;
+    if (granularity != FP8G_SCALE_PER_ROW && granularity != FP8G_SCALE_PER_TENSOR) return FP8G_ERR_DTYPE;
+    const bool per_tensor = granularity == FP8G_SCALE_PER_TENSOR;
+    if (!per_tensor && rows == 0) return FP8G_OK;
+    const int64_t n = mul3(rows, cols, 1);
+    if (n < 0 || n > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (!scale) return FP8G_ERR_NULL;
+    if (n > 0 && (!x || !q)) return FP8G_ERR_NULL;
+    if (!aligned16(scale) || (x && !aligned16(x)) || (q && !aligned16(q))) return FP8G_ERR_ALIGN;
+    const int64_t esz = in_dtype == FP8G_IN_BF16 ? 2 : 4;
+    const Range rx = range_of(x, n * esz), rq = range_of(q, n), rs = range_of(scale, per_tensor ? 4 : rows * 4);
+    if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return FP8G_ERR_OVERLAP;
+    return hip_status(fp8g::launch_quantize(x, in_dtype == FP8G_IN_BF16, rows, cols, per_tensor, q, scale, stream));
+}
+
 int mxfp8_quantize(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale, hipStream_t stream) {
     if (rows < 0 || cols < 0 || cols % 32 != 0) return FP8G_ERR_SHAPE;
     const int64_t n = mul3(rows, cols, 1);
@@ -127,7 +145,7 @@ const char* fp8g_status_string(int status) {
         case FP8G_ERR_NULL: return "a required pointer is NULL";
         case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k / cols not a multiple of 32 for MXFP8)";
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case FP8G_ERR_DTYPE: return "unknown output dtype or element size";
+        case FP8G_ERR_DTYPE: return "unknown output dtype, input dtype, granularity or element size";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
         case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (k % 16 for fp8_gemm_scaled, or size overflow)";
         case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";

@@ -5,6 +5,8 @@
  *
  * Operations (definitions in each entry point's comment):
  *   fp8_quantize_rowwise  fp32 [rows, cols] -> E4M3 codes + one fp32 scale per row
+ *   fp8_quantize_ex       the same quantizer for fp32 or bf16 input, with one
+ *                         scale per row or one per tensor
  *   mxfp8_quantize        fp32 [rows, cols] -> E4M3 codes + one UE8M0 scale per
  *                         32 consecutive elements of a row (MXFP8)
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
@@ -44,11 +46,21 @@ typedef enum {
 } fp8g_out_t;
 
 typedef enum {
+    FP8G_IN_F32 = 0,  /* float32 input */
+    FP8G_IN_BF16 = 1  /* bfloat16 input (converted to float32 exactly) */
+} fp8g_in_t;
+
+typedef enum {
+    FP8G_SCALE_PER_ROW = 0,    /* one scale per row: scale [rows] */
+    FP8G_SCALE_PER_TENSOR = 1  /* one scale for the whole tensor: scale [1] */
+} fp8g_granularity_t;
+
+typedef enum {
     FP8G_OK = 0,
     FP8G_ERR_NULL = 1,        /* required pointer is NULL */
     FP8G_ERR_SHAPE = 2,       /* negative extent, or k not a multiple of 32 for MXFP8 */
     FP8G_ERR_ALIGN = 3,       /* pointer not 16-byte aligned */
-    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype or element size */
+    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype, input dtype, granularity or element size */
     FP8G_ERR_OVERLAP = 5,     /* an output overlaps an input or another output */
     FP8G_ERR_UNSUPPORTED = 6, /* valid but outside this build's limits (see each call) */
     FP8G_ERR_HIP = 7          /* the HIP runtime refused the launch */
@@ -108,6 +120,35 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
                     const uint8_t* A, const uint8_t* B,
                     const float* scale_a, const float* scale_b,
                     void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * fp8_quantize_ex -- E4M3 quantization with the scale rule of
+ * fp8_quantize_rowwise, for fp32 or bf16 input, per row or per tensor.
+ *
+ * Source: the scale rule abs_max / 448 in `_calibrate_scales` of the
+ * hybrid-inference class on the page "FP8 推理基础设施（五）：从 DeepGEMM 到
+ * vLLM", which takes abs_max over a whole tensor (per tensor); per row as in
+ * fp8_quantize_rowwise.  bf16 is the precision models are usually deployed in
+ * (page on FP8 vLLM for AMD Instinct, introduction); each bf16 value is
+ * converted to fp32 exactly (its bits shifted up by 16), so the result is that
+ * of the fp32 quantizer on the converted tensor.
+ *
+ *   per row:    s[r] = fp32(max_c |x[r,c]| / 448),  q[r,c] = E4M3_RNE_SAT(fp32(x[r,c] / s[r]))
+ *   per tensor: s[0] = fp32(max_{r,c} |x[r,c]| / 448), q[r,c] = E4M3_RNE_SAT(fp32(x[r,c] / s[0]))
+ *   a zero scale gives signed zeros, as in fp8_quantize_rowwise.
+ *
+ * x        device, [rows, cols] of in_dtype (FP8G_IN_F32 / FP8G_IN_BF16), read only
+ * q        device, E4M3 codes [rows, cols], written
+ * scale    device, fp32, written: [rows] (FP8G_SCALE_PER_ROW) or [1]
+ *          (FP8G_SCALE_PER_TENSOR; it holds an intermediate until the call's
+ *          work on the stream has finished)
+ * rows, cols >= 0.  Per row: rows == 0 is a no-op.  Per tensor: the scale is
+ * always written (0 for an empty tensor).  Bit-exact with the definition.
+ * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_DTYPE (unknown in_dtype or
+ * granularity), ERR_ALIGN, ERR_OVERLAP, ERR_UNSUPPORTED (size overflow), ERR_HIP.
+ */
+int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int granularity,
+                    uint8_t* q, float* scale, hipStream_t stream);
 
 /*
  * mxfp8_quantize -- MXFP8 block quantization (the step before mxfp8_gemm).

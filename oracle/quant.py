@@ -58,6 +58,27 @@ def quantize_rowwise(x):
     return e4m3.encode(y), s
 
 
+def bf16_to_f32(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to float32: bf16 is the top half of an
+    fp32, so the value converts exactly by shifting its bits up by 16."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def quantize_tensorwise(x):
+    """Per-tensor E4M3 quantization: one scale for the whole tensor, the
+    amax/448 of `_calibrate_scales` on the DeepGEMM page (abs_max over the data).
+    Returns (codes uint8 [same shape], scale fp32 [1])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(E4M3_MAX))               # IEEE fp32 divide
+    if s == 0:
+        y = np.copysign(np.float32(0.0), x).astype(np.float32)
+    else:
+        y = (x / s).astype(np.float32)                        # IEEE fp32 divide, round to nearest
+    return e4m3.encode(y), np.array([s], dtype=np.float32)
+
+
 def mx_block_exponent(amax) -> np.ndarray:
     """Smallest integer e with amax <= 448 * 2^e, clamped to [-127, 127].
 

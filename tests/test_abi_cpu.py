@@ -27,8 +27,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
-    assert set(names) == {"fp8_quantize_rowwise", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
-                          "concat_mla_k", "fp8g_status_string"}
+    assert set(names) == {"fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled",
+                          "mxfp8_gemm", "concat_mla_k", "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -106,6 +106,32 @@ def test_quantize_argument_checks(lib):
     assert quant(lib, q=P_(64)) == OVERLAP                    # q inside x
     assert quant(lib, s=P_((1 << 30) + 16)) == OVERLAP        # scale inside q
     assert quant(lib, cols=0, x=None, q=None) in (OK, HIP)    # empty rows: only scales written
+
+
+def qex(lib, x=P_(0), dt=0, rows=8, cols=64, g=0, q=P_(1 << 30), s=P_(2 << 30)):
+    return lib.fp8_quantize_ex(x, dt, rows, cols, g, q, s, ctypes.c_void_p(S))
+
+
+def test_quantize_ex_argument_checks(lib):
+    for g in (0, 1):
+        assert qex(lib, rows=-1, g=g) == SHAPE
+        assert qex(lib, cols=-1, g=g) == SHAPE
+        assert qex(lib, s=None, g=g) == NULL
+        assert qex(lib, x=None, g=g) == NULL
+        assert qex(lib, q=None, g=g) == NULL
+        assert qex(lib, x=P_(8), g=g) == ALIGN
+        assert qex(lib, s=P_((2 << 30) + 4), g=g) == ALIGN
+        assert qex(lib, q=P_(256), g=g) == OVERLAP                       # q inside x (fp32: 2 KB)
+    assert qex(lib, dt=2) == DTYPE
+    assert qex(lib, dt=-1) == DTYPE
+    assert qex(lib, g=2) == DTYPE
+    assert qex(lib, rows=0, x=None, q=None, s=None) == OK                # per row, empty: no-op
+    assert qex(lib, rows=0, x=None, q=None, s=None, g=1) == NULL         # per tensor: the scale is written
+    assert qex(lib, rows=0, x=None, q=None, g=1) in (OK, HIP)
+    assert qex(lib, dt=1, q=P_(1024)) in (OK, HIP)                       # bf16: x is 1 KB, q adjacent
+    assert qex(lib, dt=1, q=P_(1008)) == OVERLAP
+    assert qex(lib, g=1, s=P_((1 << 30) + 496)) == OVERLAP               # scale [1] inside q
+    assert qex(lib, rows=1 << 40, cols=1 << 30) == UNSUPPORTED
 
 
 def mxq(lib, x=P_(0), rows=8, cols=64, q=P_(1 << 30), s=P_(2 << 30)):

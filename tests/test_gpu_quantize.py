@@ -7,6 +7,7 @@ import pytest
 
 import synth
 from gpu_util import oracle_quantize_rows, say, to_dev, to_host
+from oracle import quant
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +169,87 @@ def test_quantize_deterministic(gpu_lib):
     q2, s2 = gpu_lib.fp8_quantize_rowwise(x)
     import torch
     assert torch.equal(q1.view(torch.uint8), q2.view(torch.uint8)) and torch.equal(s1, s2)
+
+
+# ---- fp8_quantize_ex: bf16 input, and one scale per tensor
+
+def _bf16_bits(x32):
+    """fp32 -> bf16 bit patterns (round to nearest even), via torch on the CPU."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+BF16_SHAPES = [(1, 8), (3, 16), (7, 512), (5, 520), (130, 2048), (9, 4096), (4, 8192), (3, 16384), (2, 32776),
+               (6, 1000), (5, 257), (2, 3)]
+
+
+@pytest.mark.parametrize("rows,cols", BF16_SHAPES)
+def test_quantize_bf16_rows(gpu_lib, rows, cols):
+    """bf16 rows through every kernel variant (8 elements per 16-byte load, the
+    two-pass path, the element-wise path): codes and scales equal the oracle's
+    row-wise quantizer on the exactly converted fp32 tensor."""
+    w = synth.Workload("qb", rows, rows, cols, "a", "rowfactor_outlier", "normal", "rowwise", 23)
+    bits = _bf16_bits(synth.draw(w, "a"))
+    say("quantize bf16 rows", rows, cols)
+    q, s = gpu_lib.fp8_quantize_ex(_dev_bf16(bits))
+    qr, sr = quant.quantize_rowwise(quant.bf16_to_f32(bits))
+    assert np.array_equal(to_host(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(to_host(q), qr)
+
+
+def test_quantize_bf16_edge_rows(gpu_lib):
+    bits = _bf16_bits(edge_rows(64))
+    q, s = gpu_lib.fp8_quantize_ex(_dev_bf16(bits))
+    qr, sr = quant.quantize_rowwise(quant.bf16_to_f32(bits))
+    assert np.array_equal(to_host(s).view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(to_host(q), qr)
+
+
+def _tensor_cases():
+    rng_key = synth.stream_key(0x7E50, 1)
+    out = []
+    for (r, c) in [(1, 1), (3, 5), (1, 7), (33, 1001), (1000, 1001), (4096, 4096), (2, 3)]:
+        x = synth.normal(rng_key, 0, r * c).astype(np.float32).reshape(r, c)
+        out.append(("normal %dx%d" % (r, c), x))
+    x = synth.normal(rng_key, 0, 999 * 17).astype(np.float32).reshape(999, 17)
+    x[-1, -1] = 1.0e6                                   # amax in the scalar tail (past the last whole vector)
+    out.append(("amax in tail", x))
+    x = synth.normal(rng_key, 0, 512 * 2048).astype(np.float32).reshape(512, 2048)
+    x[300, 1000] = -3.0e5                               # amax in the middle, negative
+    out.append(("amax in middle", x))
+    out.append(("all zero", np.zeros((64, 64), np.float32)))
+    return out
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_quantize_per_tensor(gpu_lib, in_dtype):
+    """One scale for the tensor: the amax of every element across all
+    workgroups (atomic max) and the cast with it, bit-exact vs the oracle."""
+    for name, x in _tensor_cases():
+        say("quantize per tensor", in_dtype, name, x.shape)
+        if in_dtype == "bf16":
+            bits = _bf16_bits(x)
+            xin, x32 = _dev_bf16(bits), quant.bf16_to_f32(bits)
+        else:
+            xin, x32 = to_dev(x), x
+        q, s = gpu_lib.fp8_quantize_ex(xin, per_tensor=True)
+        qr, sr = quant.quantize_tensorwise(x32)
+        assert np.array_equal(to_host(s).view(np.uint32), sr.view(np.uint32)), (name, to_host(s), sr)
+        qg = to_host(q)
+        if not np.array_equal(qg, qr):
+            i = np.argwhere(qg != qr)[0]
+            raise AssertionError("%s: %d codes differ, first at %s" % (name, int((qg != qr).sum()), tuple(i)))
+
+
+def test_quantize_ex_fp32_rows_equal_rowwise(gpu_lib):
+    """fp8_quantize_ex on fp32 rows is fp8_quantize_rowwise."""
+    w = synth.WORKLOADS["c3_8192x2048x8192"]
+    x = to_dev(synth.draw(w, "b", slice(0, 512)))
+    q1, s1 = gpu_lib.fp8_quantize_rowwise(x)
+    q2, s2 = gpu_lib.fp8_quantize_ex(x)
+    assert np.array_equal(to_host(q1), to_host(q2)) and np.array_equal(to_host(s1), to_host(s2))

@@ -154,3 +154,40 @@ def test_mx_zero_block():
 def test_mx_rejects_ragged_k():
     with pytest.raises(ValueError):
         quant.mx_quantize(np.zeros((1, 33), np.float32))
+
+
+def test_bf16_to_f32_matches_torch_every_pattern():
+    """All 65536 bfloat16 patterns against torch's own bf16 -> fp32 conversion
+    (NaN patterns compared as NaN)."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    got = quant.bf16_to_f32(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_tensorwise_power_of_two_example():
+    # amax 896 over the whole tensor -> s = 2; codes are those of x / 2 in the
+    # format table (hand-derived as in test_power_of_two_scale_row)
+    x = np.array([[1.0, -3.0, 0.5], [2.0 ** -8, 896.0, -2.0 ** -12]], dtype=np.float32)
+    q, s = quant.quantize_tensorwise(x)
+    assert s.tolist() == [2.0]
+    assert q.tolist() == [[0x30, 0xBC, 0x28], [0x01, 0x7E, 0x80]]
+
+
+def test_tensorwise_is_rowwise_of_the_flattened_tensor():
+    # one scale for all elements = the row-wise rule applied to a single row
+    w = synth.Workload("t", 37, 37, 300, "a", "rowfactor_outlier", "normal", "rowwise", 21)
+    x = synth.draw(w, "a")
+    q, s = quant.quantize_tensorwise(x)
+    qr, sr = quant.quantize_rowwise(x.reshape(1, -1))
+    assert np.array_equal(q.reshape(1, -1), qr) and np.array_equal(s, sr)
+
+
+def test_tensorwise_zero_and_empty():
+    q, s = quant.quantize_tensorwise(np.array([[0.0, -0.0]], np.float32))
+    assert s.tolist() == [0.0] and q.tolist() == [[0x00, 0x80]]
+    q, s = quant.quantize_tensorwise(np.zeros((0, 5), np.float32))
+    assert s.tolist() == [0.0] and q.shape == (0, 5)
