@@ -255,3 +255,99 @@ def test_alignment_term_bounds_the_model():
     assert _emulate_group_alignment(a2, b2) == Fraction(1024125, 1000)
     a3 = np.array([0x60] + [0] * 7 + [0x18] + [0] * 7, np.uint8)   # the small product in the next run
     assert _emulate_group_alignment(a3, a3) == 1024 + Fraction(1, 256)
+
+
+# ---- E5M2 operands (oracle.e5m2): the float64 sum rounds, within K * 2^-53 * W
+
+from oracle import e5m2  # noqa: E402
+
+FMT_PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+
+
+def _finite_codes(seed, shape, fmt):
+    c = synth.u8_codes(seed, 1, shape, exclude_nan=False)
+    if fmt == "e5m2":
+        return np.where((c & 0x7C) == 0x7C, c & 0xF3, c).astype(np.uint8)   # drop Inf/NaN exponents
+    return np.where((c & 0x7F) == 0x7F, c ^ 1, c).astype(np.uint8)
+
+
+def _frac(c, fmt):
+    return Fraction((e5m2 if fmt == "e5m2" else e4m3).decode_code(int(c)))
+
+
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 3, 64), (3, 2, 48)])
+def test_mode_a_rational_brute_force_e5m2(fa, fb, M, N, K):
+    A = _finite_codes(700 + K, (M, K), fa)
+    B = _finite_codes(800 + K, (N, K), fb)
+    assert (e5m2.decode(A if fa == "e5m2" else B) != 0).any()
+    sa = synth.scales(synth.WORKLOADS["c1_128x256x512"], "a")[:M]
+    sb = synth.scales(synth.WORKLOADS["c1_128x256x512"], "b")[:N]
+    D = gemm.gemm_scaled(A, B, sa, sb, fa, fb)
+    W = gemm.gemm_scaled_weight(A, B, sa, sb, fa, fb)
+    for m in range(M):
+        for n in range(N):
+            terms = [_frac(A[m, k], fa) * _frac(B[n, k], fb) for k in range(K)]
+            s = Fraction(float(sa[m])) * Fraction(float(sb[n]))
+            exact = sum(terms) * s
+            absw = sum(abs(t) for t in terms) * abs(s)
+            assert abs(Fraction(D[m, n]) - exact) <= (K + 2) * Fraction(1, 2 ** 53) * absw
+            assert abs(Fraction(W[m, n]) - absw) <= (K + 2) * Fraction(1, 2 ** 53) * absw
+
+
+@pytest.mark.parametrize("fa,fb", FMT_PAIRS)
+def test_mode_b_rational_brute_force_e5m2(fa, fb):
+    M, N, K = 2, 3, 96
+    A = _finite_codes(900, (M, K), fa)
+    B = _finite_codes(901, (N, K), fb)
+    ea = synth.u8_codes(7, 2, (M, K // 32)) % 40 + 107
+    eb = synth.u8_codes(8, 3, (N, K // 32)) % 40 + 107
+    D = gemm.mxfp8_gemm(A, B, ea, eb, fa, fb)
+    for m in range(M):
+        for n in range(N):
+            terms = [Fraction(2) ** (int(ea[m, k // 32]) + int(eb[n, k // 32]) - 254)
+                     * _frac(A[m, k], fa) * _frac(B[n, k], fb) for k in range(K)]
+            absw = sum(abs(t) for t in terms)
+            assert abs(Fraction(D[m, n]) - sum(terms)) <= (K + 2) * Fraction(1, 2 ** 53) * absw
+
+
+def test_e5m2_product_table_every_code_pair():
+    """Every pair of finite E5M2 codes, and every E4M3 x E5M2 pair, as a K=1
+    product against torch's decode of both formats (products of 3-bit
+    significands are exact in float64)."""
+    c = np.arange(256, dtype=np.uint8)
+    f5 = c[e5m2.is_finite_code(c)]
+    f4 = c[e4m3.is_finite_code(c)]
+    t5 = torch.from_numpy(f5).view(torch.float8_e5m2).to(torch.float64).numpy()
+    t4 = torch.from_numpy(f4).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    one5, one4 = np.ones(f5.size, np.float32), np.ones(f4.size, np.float32)
+    D = gemm.gemm_scaled(f5[:, None], f5[:, None], one5, one5, "e5m2", "e5m2")
+    assert np.array_equal(D, np.outer(t5, t5))
+    D = gemm.gemm_scaled(f4[:, None], f5[:, None], one4, one5, "e4m3", "e5m2")
+    assert np.array_equal(D, np.outer(t4, t5))
+    with pytest.raises(ValueError):
+        gemm.gemm_scaled(np.array([[0x7C]], np.uint8), np.array([[0x3C]], np.uint8), one5[:1], one5[:1],
+                         "e5m2", "e5m2")
+
+
+def test_e5m2_ones_closed_form():
+    """1.0 is 0x3C in E5M2: an all-ones product is K * sa * sb, also with an
+    E4M3 1.0 (0x38) on the other side."""
+    K = 1000
+    A = np.full((2, K), 0x3C, np.uint8)
+    B4 = np.full((3, K), 0x38, np.uint8)
+    sa, sb = np.array([0.5, 3.0], np.float32), np.array([1.0, 2.0, 0.25], np.float32)
+    assert np.array_equal(gemm.gemm_scaled(A, B4, sa, sb, "e5m2", "e4m3"), K * np.outer(sa, sb).astype(np.float64))
+
+
+def test_alignment_term_e5m2_exponents():
+    # 1.0 -> 0, max 57344 -> 15, min normal and every subnormal or zero -> -14
+    c = np.array([0x3C, 0x7B, 0x04, 0x01, 0x00, 0x80, 0xBF], np.uint8)
+    assert list(gemm.code_exponent(c, "e5m2")) == [0, 15, -14, -14, -14, -14, 0]
+    Z = np.zeros((1, 16), np.uint8)                # two all-zero runs: exponent -14 each
+    assert gemm.alignment_term(Z, Z, fmt_a="e5m2", fmt_b="e5m2")[0, 0] == 2 * 7 * 2.0 ** (-28 - 13)
+    A = np.zeros((1, 8), np.uint8)
+    A[0, 0] = 0x50                                 # 32 = 2^5 in E5M2
+    B = np.zeros((1, 8), np.uint8)
+    B[0, 0] = 0x60                                 # 32 = 2^5 in E4M3
+    assert gemm.alignment_term(A, B, fmt_a="e5m2", fmt_b="e4m3")[0, 0] == 7 * 2.0 ** (10 - 13)
