@@ -1,4 +1,4 @@
-"""fp8g -- FP8 (E4M3) scaled GEMM and row-wise quantizer for MI355X (gfx950).
+"""fp8g -- FP8 scaled GEMM and quantizers for MI355X (gfx950).
 
 Thin Python binding over the C ABI in ``include/fp8g.h`` (libfp8g.so, built
 in-tree by ``python -m fp8_scaled_gemm_amd.build``).  Every computation runs in
@@ -13,24 +13,29 @@ Functions keep the C names and argument order:
     mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
+    fp8_gemm_scaled_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b)  -> D
+    mxfp8_gemm_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b)       -> D
+                                            (fmt: FMT_E4M3 or FMT_E5M2 per operand)
     concat_mla_k(k_nope, k_rope)                         -> k  (MLA key rows)
 
-E4M3 tensors are ``torch.float8_e4m3fn`` (OCP, the gfx950 format) or raw
-``torch.uint8`` codes; the FNUZ variant of gfx942 is rejected.
+E4M3 tensors are ``torch.float8_e4m3fn`` (OCP, the gfx950 format) and E5M2
+tensors ``torch.float8_e5m2``, or either as raw ``torch.uint8`` codes; the
+FNUZ variants of gfx942 are rejected.
 """
 
 import ctypes
 import os
 import re
 
-__all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm", "concat_mla_k",
-           "status_string",
-           "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32"]
+__all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
+           "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k", "status_string",
+           "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32", "FMT_E4M3", "FMT_E5M2"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8g.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp8g.h")
 OUT_BF16, OUT_F32 = 0, 1
+FMT_E4M3, FMT_E5M2 = 0, 1
 
 _lib = None
 
@@ -42,6 +47,10 @@ _SIGNATURES = {
     "fp8_quantize_ex": [_VOIDP, ctypes.c_int, _I64, _I64, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
+    "fp8_gemm_scaled_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
+                           ctypes.c_int, _VOIDP],
+    "mxfp8_gemm_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
+                      ctypes.c_int, _VOIDP],
     "concat_mla_k": [_VOIDP, _VOIDP, _VOIDP, _I64, _I64, _I64, ctypes.c_int, _VOIDP],
 }
 
@@ -100,15 +109,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
 
 
-def _as_codes(t, name):
+def _as_codes(t, name, fmt=FMT_E4M3):
+    """uint8 view of an operand of format fmt (its float8 dtype or raw codes)."""
     torch = _torch()
-    if t.dtype == torch.float8_e4m3fn:
+    want = {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}.get(fmt)
+    if want is None:
+        raise ValueError("%s: format must be FMT_E4M3 or FMT_E5M2, got %r" % (name, fmt))
+    if t.dtype == want:
         return t.view(torch.uint8)
     if t.dtype == torch.uint8:
         return t
-    if t.dtype == getattr(torch, "float8_e4m3fnuz", None):
-        raise TypeError("%s: float8_e4m3fnuz (gfx942) is not the OCP E4M3FN format used on gfx950" % name)
-    raise TypeError("%s must be float8_e4m3fn or uint8 codes, got %s" % (name, t.dtype))
+    if t.dtype in (getattr(torch, "float8_e4m3fnuz", None), getattr(torch, "float8_e5m2fnuz", None)):
+        raise TypeError("%s: %s (gfx942) is not an OCP format used on gfx950" % (name, t.dtype))
+    raise TypeError("%s must be %s or uint8 codes, got %s" % (name, want, t.dtype))
 
 
 def _need(t, name, dtype=None, shape=None):
@@ -208,8 +221,8 @@ def mxfp8_quantize(x, q=None, scale=None):
     return q, scale
 
 
-def _gemm_operands(m, n, k, A, B):
-    Ac, Bc = _as_codes(A, "A"), _as_codes(B, "B")
+def _gemm_operands(m, n, k, A, B, fmt_a=FMT_E4M3, fmt_b=FMT_E4M3):
+    Ac, Bc = _as_codes(A, "A", fmt_a), _as_codes(B, "B", fmt_b)
     _need(Ac, "A", shape=(m, k))
     _need(Bc, "B", shape=(n, k))
     return Ac, Bc
@@ -224,8 +237,22 @@ def _out(m, n, A, D, out_dtype):
     return D, code
 
 
+def fp8_gemm_scaled_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b, D=None, out_dtype=None):
+    """D[m,n] = scale_a[m] * scale_b[n] * sum_k A[m,k] * B[n,k] with A of format
+    fmt_a and B of format fmt_b (FMT_E4M3 / FMT_E5M2)."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    Ac, Bc = _gemm_operands(m, n, k, A, B, fmt_a, fmt_b)
+    _need(scale_a, "scale_a", torch.float32, (m,))
+    _need(scale_b, "scale_b", torch.float32, (n,))
+    D, code = _out(m, n, A, D, out_dtype)
+    _check(load().fp8_gemm_scaled_ex(m, n, k, _ptr(Ac), fmt_a, _ptr(Bc), fmt_b, _ptr(scale_a), _ptr(scale_b),
+                                     _ptr(D), code, _stream()), "fp8_gemm_scaled_ex")
+    return D
+
+
 def fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
-    """D[m,n] = scale_a[m] * scale_b[n] * sum_k A[m,k] * B[n,k] (A [m,k], B [n,k])."""
+    """D[m,n] = scale_a[m] * scale_b[n] * sum_k A[m,k] * B[n,k] (A [m,k], B [n,k], E4M3)."""
     torch = _torch()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     Ac, Bc = _gemm_operands(m, n, k, A, B)
@@ -237,15 +264,33 @@ def fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
     return D
 
 
+def _mx_scales(m, n, k, scale_a, scale_b):
+    torch = _torch()
+    if k % 32:
+        raise ValueError("k must be a multiple of 32 for MXFP8")
+    _need(scale_a, "scale_a", torch.uint8, (m, k // 32))
+    _need(scale_b, "scale_b", torch.uint8, (n, k // 32))
+
+
+def mxfp8_gemm_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b, D=None, out_dtype=None):
+    """MX GEMM with A of format fmt_a and B of format fmt_b (FMT_E4M3 / FMT_E5M2);
+    scale_a [m, k/32] and scale_b [n, k/32] are UE8M0 codes (uint8)."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    Ac, Bc = _gemm_operands(m, n, k, A, B, fmt_a, fmt_b)
+    _mx_scales(m, n, k, scale_a, scale_b)
+    D, code = _out(m, n, A, D, out_dtype)
+    _check(load().mxfp8_gemm_ex(m, n, k, _ptr(Ac), fmt_a, _ptr(Bc), fmt_b, _ptr(scale_a), _ptr(scale_b), _ptr(D),
+                                code, _stream()), "mxfp8_gemm_ex")
+    return D
+
+
 def mxfp8_gemm(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
     """MXFP8 GEMM: scale_a [m, k/32] and scale_b [n, k/32] are UE8M0 codes (uint8)."""
     torch = _torch()
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     Ac, Bc = _gemm_operands(m, n, k, A, B)
-    if k % 32:
-        raise ValueError("k must be a multiple of 32 for MXFP8")
-    _need(scale_a, "scale_a", torch.uint8, (m, k // 32))
-    _need(scale_b, "scale_b", torch.uint8, (n, k // 32))
+    _mx_scales(m, n, k, scale_a, scale_b)
     D, code = _out(m, n, A, D, out_dtype)
     _check(load().mxfp8_gemm(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D), code,
                              _stream()), "mxfp8_gemm")

@@ -55,6 +55,8 @@ int check_gemm_common(int64_t m, int64_t n, int64_t k, const void* A, const void
     return -1;  // go on
 }
 
+bool valid_fmt(int f) { return f == FP8G_FMT_E4M3 || f == FP8G_FMT_E5M2; }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8G_OK : FP8G_ERR_HIP; }
 
 }  // namespace
@@ -105,21 +107,35 @@ int mxfp8_quantize(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8
     return hip_status(fp8g::launch_quantize_mx(x, rows, cols, q, scale, stream));
 }
 
-int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* scale_a,
-                    const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
+int fp8_gemm_scaled_ex(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                       const float* scale_a, const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 0) return FP8G_ERR_SHAPE;
+    if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b)) return FP8G_ERR_DTYPE;
     const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * 4, n * 4, D, out_dtype);
     if (st >= 0) return st;
     if (k % 16 != 0) return FP8G_ERR_UNSUPPORTED;
-    return hip_status(fp8g::launch_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D,
+    return hip_status(fp8g::launch_gemm_scaled(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b, D,
                                                out_dtype == FP8G_OUT_F32, stream));
+}
+
+int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* scale_a,
+                    const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    return fp8_gemm_scaled_ex(m, n, k, A, FP8G_FMT_E4M3, B, FP8G_FMT_E4M3, scale_a, scale_b, D, out_dtype, stream);
+}
+
+int mxfp8_gemm_ex(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                  const uint8_t* scale_a, const uint8_t* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return FP8G_ERR_SHAPE;
+    if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b)) return FP8G_ERR_DTYPE;
+    const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * (k / 32), n * (k / 32), D, out_dtype);
+    if (st >= 0) return st;
+    return hip_status(fp8g::launch_gemm_mx(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b, D,
+                                           out_dtype == FP8G_OUT_F32, stream));
 }
 
 int mxfp8_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const uint8_t* scale_a,
                const uint8_t* scale_b, void* D, int out_dtype, hipStream_t stream) {
-    if (m >= 0 && n >= 0 && k >= 0 && k % 32 != 0) return FP8G_ERR_SHAPE;
-    const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * (k / 32), n * (k / 32), D, out_dtype);
-    if (st >= 0) return st;
-    return hip_status(fp8g::launch_gemm_mx(m, n, k, A, B, scale_a, scale_b, D, out_dtype == FP8G_OUT_F32, stream));
+    return mxfp8_gemm_ex(m, n, k, A, FP8G_FMT_E4M3, B, FP8G_FMT_E4M3, scale_a, scale_b, D, out_dtype, stream);
 }
 
 int concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens, int64_t heads,

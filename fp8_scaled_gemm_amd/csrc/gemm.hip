@@ -1,4 +1,5 @@
-// FP8 (E4M3) scaled GEMM on the gfx950 matrix cores, two scaling modes.
+// FP8 scaled GEMM on the gfx950 matrix cores, two scaling modes, each operand
+// E4M3 or E5M2.
 //
 //   mode (a)  D[m,n] = sa[m] sb[n] sum_k A[m,k] B[n,k]
 //             per-token / per-channel fp32 scales, as the DeepGEMM call on the
@@ -6,6 +7,11 @@
 //   mode (b)  D[m,n] = sum_j 2^(ea[m,j]-127) 2^(eb[n,j]-127) sum_{t<32} A[m,32j+t] B[n,32j+t]
 //             MXFP8: one UE8M0 scale per 32 K elements of every row, as on the
 //             page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm 통합", sections 1-2.
+//
+// Operand formats: the matrix-core instruction takes a format per operand
+// (E4M3 = "fp8", E5M2 = "bf8"), so each of A and B may be either; the format
+// pair is a template parameter and changes nothing else (a zero byte is +0 in
+// both, so the zero-filled K tail is the same).
 //
 // Both operands are K-major bytes (A [M,K], B [N,K]).  The work is a dense
 // contraction (2MNK flops at arithmetic intensity in the thousands), so it is
@@ -161,7 +167,9 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
 
 // ---------------------------------------------------------------- kernel
 
-template <bool MX, bool OUT_F32, bool KTAIL>
+// FA, FB: format code of A and of B (0 = E4M3, 1 = E5M2, as the instruction's
+// format fields)
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const float* __restrict__ sa, const float* __restrict__ sb, const uint8_t* __restrict__ ea,
@@ -309,11 +317,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // The empty asm after each step pins it where it is written: the builtin has
     // no side effects, so without it the optimizer may sink whole stages of
     // steps past later barriers, leaving the matrix core idle in between.
+    // The instruction's first operand is fed from B's rows, so its format
+    // field is FB and the second one's FA.
     auto mfma = [&](v16f& c, const v8i& fbi, const v8i& faj, uint32_t sbi, uint32_t saj) __attribute__((always_inline)) {
         if constexpr (MX)
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, 0, 0, 0, (int)sbi, 0, (int)saj);
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, FB, FA, 0, (int)sbi, 0, (int)saj);
         else
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, 0, 0, 0, 127, 0, 127);
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, FB, FA, 0, 127, 0, 127);
         asm volatile("" : "+a"(c));
     };
 
@@ -655,11 +665,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     wait_vmcnt<0>();   // the past-the-end loads must land before the workgroup exits
 }
 
-template <bool MX, bool OUT_F32, bool KTAIL>
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB>
 static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
                              hipStream_t stream) {
-    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL>;
+    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB>;
     constexpr int LDS_BYTES = Ring<MX, KTAIL>::LDS_TOTAL;
     // up to 160 KB of dynamic LDS is above the default launch limit; raise it once.
     static std::once_flag once;
@@ -681,18 +691,63 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
     return hipGetLastError();
 }
 
-template <bool MX>
-static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
-                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
-                              int out_f32, hipStream_t stream) {
+template <bool MX, int FA, int FB>
+hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
+                      const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
+                      hipStream_t stream) {
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
     if (out_f32)
-        return tail ? launch_one<MX, true, true>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
-                    : launch_one<MX, true, false>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
-    return tail ? launch_one<MX, false, true>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
-                : launch_one<MX, false, false>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
+        return tail ? launch_one<MX, true, true, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
+                    : launch_one<MX, true, false, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
+    return tail ? launch_one<MX, false, true, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
+                : launch_one<MX, false, false, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
+}
+
+// Each operand-format pair's kernels may be compiled in an object of their
+// own (FP8G_GEMM_FMT = 2 * FA + FB, set by the library build so that the four
+// pairs compile in parallel); the object with FP8G_GEMM_FMT 0 also holds the
+// dispatch below.  Without the macro one object holds everything.
+#ifndef FP8G_GEMM_FMT
+#define FP8G_GEMM_FMT -1
+#endif
+
+#define FP8G_FMT_PAIR(KW, FA, FB)                                                                              \
+    KW hipError_t launch_fmt<false, FA, FB>(int64_t, int64_t, int64_t, const uint8_t*, const uint8_t*,          \
+                                            const float*, const float*, const uint8_t*, const uint8_t*, void*,  \
+                                            int, hipStream_t);                                                  \
+    KW hipError_t launch_fmt<true, FA, FB>(int64_t, int64_t, int64_t, const uint8_t*, const uint8_t*,           \
+                                           const float*, const float*, const uint8_t*, const uint8_t*, void*,   \
+                                           int, hipStream_t);
+
+#if FP8G_GEMM_FMT >= 0
+FP8G_FMT_PAIR(extern template, 0, 0)
+FP8G_FMT_PAIR(extern template, 0, 1)
+FP8G_FMT_PAIR(extern template, 1, 0)
+FP8G_FMT_PAIR(extern template, 1, 1)
+#endif
+#if FP8G_GEMM_FMT == 0
+FP8G_FMT_PAIR(template, 0, 0)
+#elif FP8G_GEMM_FMT == 1
+FP8G_FMT_PAIR(template, 0, 1)
+#elif FP8G_GEMM_FMT == 2
+FP8G_FMT_PAIR(template, 1, 0)
+#elif FP8G_GEMM_FMT == 3
+FP8G_FMT_PAIR(template, 1, 1)
+#endif
+
+#if FP8G_GEMM_FMT <= 0
+template <bool MX>
+static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
+                              int fmt_b, const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb,
+                              void* D, int out_f32, hipStream_t stream) {
+    if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return hipErrorInvalidValue;
+    if (fmt_a == 0)
+        return fmt_b == 0 ? launch_fmt<MX, 0, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream)
+                          : launch_fmt<MX, 0, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream);
+    return fmt_b == 0 ? launch_fmt<MX, 1, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream)
+                      : launch_fmt<MX, 1, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream);
 }
 
 // 32-bit buffer offsets: a 256-row panel of K bytes stays below 2^31, so the
@@ -702,16 +757,19 @@ static bool fits(int64_t m, int64_t n, int64_t k) {
     return m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 23) && tiles < (1LL << 31);
 }
 
-hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
-                              const float* sa, const float* sb, void* D, int out_f32, hipStream_t stream) {
+hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
+                              int fmt_b, const float* sa, const float* sb, void* D, int out_f32,
+                              hipStream_t stream) {
     if (!fits(m, n, k)) return hipErrorInvalidValue;
-    return launch_mode<false>(m, n, k, A, B, sa, sb, nullptr, nullptr, D, out_f32, stream);
+    return launch_mode<false>(m, n, k, A, fmt_a, B, fmt_b, sa, sb, nullptr, nullptr, D, out_f32, stream);
 }
 
-hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
-                          const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, hipStream_t stream) {
+hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
+                          int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
+                          hipStream_t stream) {
     if (!fits(m, n, k)) return hipErrorInvalidValue;
-    return launch_mode<true>(m, n, k, A, B, nullptr, nullptr, ea, eb, D, out_f32, stream);
+    return launch_mode<true>(m, n, k, A, fmt_a, B, fmt_b, nullptr, nullptr, ea, eb, D, out_f32, stream);
 }
+#endif  // FP8G_GEMM_FMT <= 0
 
 }  // namespace fp8g

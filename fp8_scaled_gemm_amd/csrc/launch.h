@@ -21,12 +21,14 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t cols, uint8_
 hipError_t launch_concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens, int64_t heads,
                                int64_t rope_heads, int elem_bytes, hipStream_t stream);
 
-// mode (a): per-token x per-channel fp32 scales
-hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
-                              const float* sa, const float* sb, void* D, int out_f32, hipStream_t stream);
+// mode (a): per-token x per-channel fp32 scales; fmt_a, fmt_b: 0 = E4M3, 1 = E5M2
+hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
+                              int fmt_b, const float* sa, const float* sb, void* D, int out_f32,
+                              hipStream_t stream);
 
 // mode (b): UE8M0 scales, one per 32 K elements of every row
-hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
-                          const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, hipStream_t stream);
+hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
+                          int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
+                          hipStream_t stream);
 
 }  // namespace fp8g

@@ -12,6 +12,8 @@
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
  *   mxfp8_gemm            same product with one power-of-two scale per 32 K
  *                         elements of every row of A and of B (MXFP8)
+ *   fp8_gemm_scaled_ex,   the two GEMMs with the format of each operand
+ *   mxfp8_gemm_ex         chosen: E4M3 or E5M2
  *   concat_mla_k          MLA key rows: 128 "nope" + 64 "rope" elements of
  *                         1-byte (E4M3 / E5M2) or 2-byte type
  *
@@ -56,11 +58,16 @@ typedef enum {
 } fp8g_granularity_t;
 
 typedef enum {
+    FP8G_FMT_E4M3 = 0, /* OCP E4M3FN: bias 7, largest magnitude 448, no infinities */
+    FP8G_FMT_E5M2 = 1  /* OCP E5M2: bias 15, largest finite 57344, IEEE-style Inf/NaN */
+} fp8g_fmt_t;
+
+typedef enum {
     FP8G_OK = 0,
     FP8G_ERR_NULL = 1,        /* required pointer is NULL */
     FP8G_ERR_SHAPE = 2,       /* negative extent, or k not a multiple of 32 for MXFP8 */
     FP8G_ERR_ALIGN = 3,       /* pointer not 16-byte aligned */
-    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype, input dtype, granularity or element size */
+    FP8G_ERR_DTYPE = 4,       /* unknown out_dtype, operand format, input dtype, granularity or element size */
     FP8G_ERR_OVERLAP = 5,     /* an output overlaps an input or another output */
     FP8G_ERR_UNSUPPORTED = 6, /* valid but outside this build's limits (see each call) */
     FP8G_ERR_HIP = 7          /* the HIP runtime refused the launch */
@@ -203,6 +210,34 @@ int mxfp8_gemm(int64_t m, int64_t n, int64_t k,
                const uint8_t* A, const uint8_t* B,
                const uint8_t* scale_a, const uint8_t* scale_b,
                void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * fp8_gemm_scaled_ex, mxfp8_gemm_ex -- the two GEMMs above with a format per
+ * operand.
+ *
+ * Source: the page on FlashInfer's concat_mla_k with FP8 inputs (sections
+ * 1-2) takes FP8 E5M2 beside E4M3; read as the OCP E5M2 format (1 sign, 5
+ * exponent bits with bias 15, 2 mantissa bits).  The gfx950 scaled
+ * matrix-core instruction takes a format per operand, so every pair is
+ * accepted: fmt_a, fmt_b are FP8G_FMT_E4M3 or FP8G_FMT_E5M2 (else ERR_DTYPE).
+ *
+ * Arguments, definitions, limits and errors as fp8_gemm_scaled / mxfp8_gemm,
+ * with dec() the decoding of each operand's own format.  fp8_gemm_scaled and
+ * mxfp8_gemm are these calls with both formats E4M3.  Infinity and NaN codes
+ * in A or B are outside the contract.  Accuracy: as fp8_gemm_scaled; with an
+ * E5M2 operand the products span 2^-32 .. 2^32 and the matrix core's
+ * alignment of 8 products to their largest exponent sum can drop more of the
+ * small ones (the library's tests state the bound they check).
+ */
+int fp8_gemm_scaled_ex(int64_t m, int64_t n, int64_t k,
+                       const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                       const float* scale_a, const float* scale_b,
+                       void* D, int out_dtype, hipStream_t stream);
+
+int mxfp8_gemm_ex(int64_t m, int64_t n, int64_t k,
+                  const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
+                  const uint8_t* scale_a, const uint8_t* scale_b,
+                  void* D, int out_dtype, hipStream_t stream);
 
 /*
  * concat_mla_k -- assemble MLA key rows from their nope and rope parts.

@@ -28,7 +28,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
     assert set(names) == {"fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled",
-                          "mxfp8_gemm", "concat_mla_k", "fp8g_status_string"}
+                          "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k",
+                          "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -39,11 +40,14 @@ def test_status_strings(lib):
     assert fp8g.status_string(99) == "unknown status"
 
 
-def gemm(lib, fn, m, n, k, A=P_(0), B=P_(1 << 30), sa=P_(2 << 30), sb=P_(3 << 30), D=P_(4 << 30), out=0):
+def gemm(lib, fn, m, n, k, A=P_(0), B=P_(1 << 30), sa=P_(2 << 30), sb=P_(3 << 30), D=P_(4 << 30), out=0,
+         fa=1, fb=0):
+    if fn.endswith("_ex"):      # the format-per-operand variants: E5M2 A, E4M3 B unless given
+        return getattr(lib, fn)(m, n, k, A, fa, B, fb, sa, sb, D, out, ctypes.c_void_p(S))
     return getattr(lib, fn)(m, n, k, A, B, sa, sb, D, out, ctypes.c_void_p(S))
 
 
-@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm"])
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex"])
 def test_gemm_argument_checks(lib, fn):
     assert gemm(lib, fn, -1, 4, 64) == SHAPE
     assert gemm(lib, fn, 4, -1, 64) == SHAPE
@@ -70,14 +74,26 @@ def test_gemm_argument_checks(lib, fn):
     assert gemm(lib, fn, 4, 4, 64, D=P_(4 * 64)) in (OK, HIP)
 
 
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled_ex", "mxfp8_gemm_ex"])
+def test_gemm_format_checks(lib, fn):
+    for fa, fb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        assert gemm(lib, fn, 4, 4, 64, fa=fa, fb=fb, D=None) == NULL     # formats accepted, checks go on
+    for fa, fb in ((2, 0), (0, 2), (-1, 0), (0, 4)):
+        assert gemm(lib, fn, 4, 4, 64, fa=fa, fb=fb) == DTYPE
+        assert gemm(lib, fn, 0, 4, 64, fa=fa, fb=fb) == DTYPE            # checked before the empty no-op
+    assert gemm(lib, fn, -1, 4, 64, fa=2) == SHAPE
+
+
 def test_mx_k_must_be_multiple_of_32(lib):
     for k in (16, 48, 33, 1):
         assert gemm(lib, "mxfp8_gemm", 4, 4, k) == SHAPE
+        assert gemm(lib, "mxfp8_gemm_ex", 4, 4, k) == SHAPE
 
 
 def test_scaled_k_must_be_multiple_of_16(lib):
     for k in (8, 24, 33, 1):
         assert gemm(lib, "fp8_gemm_scaled", 4, 4, k) == UNSUPPORTED
+        assert gemm(lib, "fp8_gemm_scaled_ex", 4, 4, k) == UNSUPPORTED
 
 
 def test_k_zero_needs_no_operands(lib):
