@@ -9,7 +9,7 @@ There is no fallback: if the library is missing, every call raises.
 Functions keep the C names and argument order:
 
     fp8_quantize_rowwise(x)                              -> (q, scale)
-    fp8_quantize_ex(x, per_tensor=False)                 -> (q, scale)  (fp32 or bf16 x)
+    fp8_quantize_ex(x, per_tensor=False, fmt=FMT_E4M3)   -> (q, scale)  (fp32 or bf16 x)
     mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
@@ -44,7 +44,7 @@ _I64 = ctypes.c_int64
 _SIGNATURES = {
     "fp8_quantize_rowwise": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
     "mxfp8_quantize": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
-    "fp8_quantize_ex": [_VOIDP, ctypes.c_int, _I64, _I64, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP],
+    "fp8_quantize_ex": [_VOIDP, ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "fp8_gemm_scaled_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
@@ -171,9 +171,10 @@ IN_F32, IN_BF16 = 0, 1
 SCALE_PER_ROW, SCALE_PER_TENSOR = 0, 1
 
 
-def fp8_quantize_ex(x, per_tensor=False, q=None, scale=None):
-    """E4M3 quantization of a 2-D fp32 or bf16 device tensor with scale
-    amax / 448, one per row (scale [R]) or one per tensor (scale [1])."""
+def fp8_quantize_ex(x, per_tensor=False, q=None, scale=None, fmt=FMT_E4M3):
+    """FP8 quantization of a 2-D fp32 or bf16 device tensor with scale
+    amax / MAX (448 for FMT_E4M3, 57344 for FMT_E5M2), one per row (scale [R])
+    or one per tensor (scale [1]).  q is float8_e4m3fn or float8_e5m2."""
     torch = _torch()
     if x.dtype == torch.float32:
         code = IN_F32
@@ -186,13 +187,16 @@ def fp8_quantize_ex(x, per_tensor=False, q=None, scale=None):
         raise ValueError("x must be 2-D")
     R, C = x.shape
     if q is None:
-        q = torch.empty((R, C), dtype=torch.float8_e4m3fn, device=x.device)
+        qdt = {FMT_E4M3: torch.float8_e4m3fn, FMT_E5M2: torch.float8_e5m2}.get(fmt)
+        if qdt is None:
+            raise ValueError("fmt must be FMT_E4M3 or FMT_E5M2, got %r" % (fmt,))
+        q = torch.empty((R, C), dtype=qdt, device=x.device)
     if scale is None:
         scale = torch.empty((1 if per_tensor else R,), dtype=torch.float32, device=x.device)
-    qc = _as_codes(q, "q")
+    qc = _as_codes(q, "q", fmt)
     _need(qc, "q", shape=(R, C))
     _need(scale, "scale", torch.float32, (1 if per_tensor else R,))
-    _check(load().fp8_quantize_ex(_ptr(x), code, R, C, SCALE_PER_TENSOR if per_tensor else SCALE_PER_ROW,
+    _check(load().fp8_quantize_ex(_ptr(x), code, R, C, SCALE_PER_TENSOR if per_tensor else SCALE_PER_ROW, fmt,
                                   _ptr(qc), _ptr(scale), _stream()), "fp8_quantize_ex")
     return q, scale
 

@@ -77,11 +77,12 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q,
     return hip_status(fp8g::launch_quantize_rowwise(x, rows, cols, q, scale, stream));
 }
 
-int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int granularity, uint8_t* q,
-                    float* scale, hipStream_t stream) {
+int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int granularity, int out_fmt,
+                    uint8_t* q, float* scale, hipStream_t stream) {
     if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
     if (in_dtype != FP8G_IN_F32 && in_dtype != FP8G_IN_BF16) return FP8G_ERR_DTYPE;
     if (granularity != FP8G_SCALE_PER_ROW && granularity != FP8G_SCALE_PER_TENSOR) return FP8G_ERR_DTYPE;
+    if (!valid_fmt(out_fmt)) return FP8G_ERR_DTYPE;
     const bool per_tensor = granularity == FP8G_SCALE_PER_TENSOR;
     if (!per_tensor && rows == 0) return FP8G_OK;
     const int64_t n = mul3(rows, cols, 1);
@@ -92,7 +93,8 @@ int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int
     const int64_t esz = in_dtype == FP8G_IN_BF16 ? 2 : 4;
     const Range rx = range_of(x, n * esz), rq = range_of(q, n), rs = range_of(scale, per_tensor ? 4 : rows * 4);
     if (overlaps(rq, rx) || overlaps(rs, rx) || overlaps(rq, rs)) return FP8G_ERR_OVERLAP;
-    return hip_status(fp8g::launch_quantize(x, in_dtype == FP8G_IN_BF16, rows, cols, per_tensor, q, scale, stream));
+    return hip_status(fp8g::launch_quantize(x, in_dtype == FP8G_IN_BF16, rows, cols, per_tensor,
+                                            out_fmt == FP8G_FMT_E5M2, q, scale, stream));
 }
 
 int mxfp8_quantize(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale, hipStream_t stream) {

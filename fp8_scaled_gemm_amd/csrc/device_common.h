@@ -20,6 +20,18 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)r;
 }
 
+// Saturating OCP E5M2 cast of four fp32 values (byte i = value i): clamped to
+// 57344 first, then the hardware convert (round to nearest even); sign of zero kept.
+__device__ __forceinline__ uint32_t e5m2_pack4(float a, float b, float c, float d) {
+    a = __builtin_fminf(__builtin_fmaxf(a, -57344.0f), 57344.0f);
+    b = __builtin_fminf(__builtin_fmaxf(b, -57344.0f), 57344.0f);
+    c = __builtin_fminf(__builtin_fmaxf(c, -57344.0f), 57344.0f);
+    d = __builtin_fminf(__builtin_fmaxf(d, -57344.0f), 57344.0f);
+    int r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);  // bytes 0,1
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);       // bytes 2,3
+    return (uint32_t)r;
+}
+
 __device__ __forceinline__ uint8_t e4m3_one(float a) {
     return (uint8_t)(e4m3_pack4(a, 0.0f, 0.0f, 0.0f) & 0xFFu);
 }

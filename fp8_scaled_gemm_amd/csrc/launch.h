@@ -9,9 +9,10 @@ namespace fp8g {
 hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                                    hipStream_t stream);
 
-// row-wise (per_tensor == 0) or per-tensor quantizer on fp32 (in_bf16 == 0) or bf16 input
-hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t cols, int per_tensor, uint8_t* q,
-                           float* scale, hipStream_t stream);
+// row-wise (per_tensor == 0) or per-tensor quantizer on fp32 (in_bf16 == 0) or bf16
+// input, to E4M3 (out_e5m2 == 0) or E5M2 codes
+hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t cols, int per_tensor, int out_e5m2,
+                           uint8_t* q, float* scale, hipStream_t stream);
 
 // MXFP8 block quantizer (cols % 32 == 0): UE8M0 scale codes [rows, cols / 32]
 hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* scale,

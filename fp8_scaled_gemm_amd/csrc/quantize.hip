@@ -1,6 +1,6 @@
-// E4M3 quantizers with a scale of amax / 448: one scale per row (per token for
-// activations, per output channel for weights), or one per tensor; fp32 or
-// bf16 input.
+// FP8 quantizers with a scale of amax / 448 (E4M3 output) or amax / 57344
+// (E5M2 output): one scale per row (per token for activations, per output
+// channel for weights), or one per tensor; fp32 or bf16 input.
 //
 // Scale rule: abs_max / 448, the E4M3 maximum (page "FP8 推理基础设施（五）：
 // 从 DeepGEMM 到 vLLM", `_calibrate_scales`, which takes abs_max over a whole
@@ -8,7 +8,9 @@
 // per-channel scale_b of the same page's DeepGEMM call (the row-wise mode).
 // bf16 input: the precision models are usually deployed in (page on FP8 vLLM
 // for AMD Instinct, introduction); a bf16 value converts to fp32 exactly, so
-// the result is that of the fp32 quantizer on the converted tensor.
+// the result is that of the fp32 quantizer on the converted tensor.  E5M2
+// output: the same rule with that format's largest finite value (57344), as
+// the page on FlashInfer's concat_mla_k with FP8 inputs takes E5M2 beside E4M3.
 //
 // HBM-bound: 4 (fp32) or 2 (bf16) bytes read + 1 byte written per element.
 // Loads are 16 bytes per lane (4 fp32 or 8 bf16 elements).  Row-wise: rows up
@@ -26,10 +28,10 @@
 // which equals RN(x / s) when y is the correctly rounded reciprocal and no
 // intermediate underflows (P. Markstein, "Computation of elementary functions
 // on the IBM RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990).  A
-// quotient small enough to underflow casts to a signed zero either way (E4M3
-// codes below 2^-10 round to zero), and scales below the smallest normal fp32
-// (where 1/s may overflow) use the IEEE division.  This file is built without
-// fast-math.
+// quotient small enough to underflow casts to a signed zero either way (values
+// below 2^-10 round to zero in E4M3, below 2^-17 in E5M2), and scales below
+// the smallest normal fp32 (where 1/s may overflow) use the IEEE division.
+// This file is built without fast-math.
 
 #include <type_traits>
 
@@ -45,6 +47,27 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 constexpr int QROWS_PER_BLOCK = 4;          // per-wave kernel: 4 waves of 64 lanes, one row each
 constexpr float FLT_MIN_NORMAL = 1.17549435e-38f;
 
+// ---- output formats: the largest finite magnitude (the divisor of amax) and
+// the saturating round-to-nearest-even cast of four values into one dword
+struct OutE4M3 {
+    static constexpr float MAX = 448.0f;
+    __device__ __forceinline__ static uint32_t pack4(float a, float b, float c, float d) {
+        return e4m3_pack4(a, b, c, d);
+    }
+};
+
+struct OutE5M2 {
+    static constexpr float MAX = 57344.0f;
+    __device__ __forceinline__ static uint32_t pack4(float a, float b, float c, float d) {
+        return e5m2_pack4(a, b, c, d);
+    }
+};
+
+template <class O>
+__device__ __forceinline__ uint8_t cast_one(float a) {
+    return (uint8_t)(O::pack4(a, 0.0f, 0.0f, 0.0f) & 0xFFu);
+}
+
 // Per-row (per-tensor) divisor: the scale, its correctly rounded reciprocal, the path.
 struct RowDiv {
     float s, y;
@@ -54,10 +77,11 @@ struct RowDiv {
 
 // amax is the same in every lane; readfirstlane makes that visible to the
 // compiler, so the path is chosen once with a scalar branch.
+template <class O>
 __device__ __forceinline__ RowDiv row_div(float amax) {
     amax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, amax)));
     RowDiv d;
-    d.s = amax / 448.0f;
+    d.s = amax / O::MAX;
     d.y = 1.0f / d.s;
     d.zero = (d.s == 0.0f);
     d.ieee = (d.s < FLT_MIN_NORMAL);
@@ -99,9 +123,9 @@ struct InF32 {
     __device__ __forceinline__ void load(const void* base, int64_t idx) { v = reinterpret_cast<const v4f*>(base)[idx]; }
     __device__ __forceinline__ void zero() { v = (v4f){0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ float amax() const { return __builtin_fmaxf(amax2(v.x, v.y), amax2(v.z, v.w)); }
-    template <int P>
+    template <class O, int P>
     __device__ __forceinline__ void store(uint8_t* q, int64_t idx, const RowDiv& d) const {
-        const uint32_t w = e4m3_pack4(quot<P>(v.x, d), quot<P>(v.y, d), quot<P>(v.z, d), quot<P>(v.w, d));
+        const uint32_t w = O::pack4(quot<P>(v.x, d), quot<P>(v.y, d), quot<P>(v.z, d), quot<P>(v.w, d));
         __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(q) + idx);
     }
     __device__ __forceinline__ static float scalar(const void* base, int64_t i) {
@@ -124,11 +148,11 @@ struct InBF16 {
         return __builtin_fmaxf(__builtin_fmaxf(amax2(lo(a), hi(a)), amax2(lo(b), hi(b))),
                                __builtin_fmaxf(amax2(lo(c), hi(c)), amax2(lo(e), hi(e))));
     }
-    template <int P>
+    template <class O, int P>
     __device__ __forceinline__ void store(uint8_t* q, int64_t idx, const RowDiv& d) const {
         const uint32_t a = r.x, b = r.y, c = r.z, e = r.w;
-        const v2u w = {e4m3_pack4(quot<P>(lo(a), d), quot<P>(hi(a), d), quot<P>(lo(b), d), quot<P>(hi(b), d)),
-                       e4m3_pack4(quot<P>(lo(c), d), quot<P>(hi(c), d), quot<P>(lo(e), d), quot<P>(hi(e), d))};
+        const v2u w = {O::pack4(quot<P>(lo(a), d), quot<P>(hi(a), d), quot<P>(lo(b), d), quot<P>(hi(b), d)),
+                       O::pack4(quot<P>(lo(c), d), quot<P>(hi(c), d), quot<P>(lo(e), d), quot<P>(hi(e), d))};
         __builtin_nontemporal_store(w, reinterpret_cast<v2u*>(q) + idx);
     }
     __device__ __forceinline__ static float scalar(const void* base, int64_t i) {
@@ -142,7 +166,7 @@ __device__ __forceinline__ const uint8_t* row_base(const void* x, int64_t row, i
 }
 
 // cols % EPL == 0, rows 16-byte aligned, cols <= 64 * VPL * EPL: one wave per row.
-template <class V, int VPL>
+template <class V, class O, int VPL>
 __global__ __launch_bounds__(256) void quantize_rows_wave(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
     const int lane = threadIdx.x & 63;
@@ -159,14 +183,14 @@ __global__ __launch_bounds__(256) void quantize_rows_wave(const void* __restrict
         if (idx < nv) v[i].load_nt(xr, idx); else v[i].zero();
         amax = __builtin_fmaxf(amax, v[i].amax());
     }
-    const RowDiv d = row_div(wave_max(amax));
+    const RowDiv d = row_div<O>(wave_max(amax));
     if (lane == 0) scale[row] = d.s;
     by_path(d, [&](auto path) {
         constexpr int P = decltype(path)::value;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
             const int64_t idx = lane + 64 * i;
-            if (idx < nv) v[i].template store<P>(qr, idx, d);
+            if (idx < nv) v[i].template store<O, P>(qr, idx, d);
         }
     });
 }
@@ -182,7 +206,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 // cols % EPL == 0, rows 16-byte aligned: one 256-thread workgroup per row.
 // VPL > 0: the row (cols <= 256 * VPL * EPL) lives in registers; VPL == 0:
 // two passes over the row (the second one mostly from cache).
-template <class V, int VPL>
+template <class V, class O, int VPL>
 __global__ __launch_bounds__(256) void quantize_rows_wg(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
     __shared__ float red[4];
@@ -207,7 +231,7 @@ __global__ __launch_bounds__(256) void quantize_rows_wg(const void* __restrict__
             amax = __builtin_fmaxf(amax, v[0].amax());
         }
     }
-    const RowDiv d = row_div(block_max(amax, red));
+    const RowDiv d = row_div<O>(block_max(amax, red));
     if (tid == 0) scale[row] = d.s;
     by_path(d, [&](auto path) {
         constexpr int P = decltype(path)::value;
@@ -215,20 +239,20 @@ __global__ __launch_bounds__(256) void quantize_rows_wg(const void* __restrict__
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int64_t idx = tid + 256 * i;
-                if (idx < nv) v[i].template store<P>(qr, idx, d);
+                if (idx < nv) v[i].template store<O, P>(qr, idx, d);
             }
         } else {
             for (int64_t idx = tid; idx < nv; idx += 256) {
                 V t;
                 t.load(xr, idx);
-                t.template store<P>(qr, idx, d);
+                t.template store<O, P>(qr, idx, d);
             }
         }
     });
 }
 
 // Any cols: element-wise loads and byte stores, two passes, one wave per row.
-template <class V>
+template <class V, class O>
 __global__ __launch_bounds__(256) void quantize_rows_scalar(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                             uint8_t* __restrict__ q, float* __restrict__ scale) {
     const int lane = threadIdx.x & 63;
@@ -237,17 +261,17 @@ __global__ __launch_bounds__(256) void quantize_rows_scalar(const void* __restri
     uint8_t* qr = q + row * cols;
     float amax = 0.0f;
     for (int64_t c = lane; c < cols; c += 64) amax = __builtin_fmaxf(amax, __builtin_fabsf(V::scalar(x, row * cols + c)));
-    const RowDiv d = row_div(wave_max(amax));
+    const RowDiv d = row_div<O>(wave_max(amax));
     if (lane == 0) scale[row] = d.s;
     by_path(d, [&](auto path) {
         constexpr int P = decltype(path)::value;
-        for (int64_t c = lane; c < cols; c += 64) qr[c] = e4m3_one(quot<P>(V::scalar(x, row * cols + c), d));
+        for (int64_t c = lane; c < cols; c += 64) qr[c] = cast_one<O>(quot<P>(V::scalar(x, row * cols + c), d));
     });
 }
 
 // ---- per tensor: n elements as one row.  The scale slot first holds the bits
 // of amax (non-negative floats order like their bit patterns, so an unsigned
-// atomic max finds it), then amax / 448.
+// atomic max finds it), then amax / MAX.
 constexpr int TQ_UNROLL = 4;
 
 __global__ void tensor_scale_clear(float* __restrict__ scale) {
@@ -278,10 +302,10 @@ __global__ __launch_bounds__(256) void tensor_amax(const void* __restrict__ x, i
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class V>
+template <class V, class O>
 __global__ __launch_bounds__(256) void tensor_quant(const void* __restrict__ x, int64_t n, uint8_t* __restrict__ q,
                                                     const float* __restrict__ slot) {
-    const RowDiv d = row_div(slot[0]);   // the slot holds amax here
+    const RowDiv d = row_div<O>(slot[0]);   // the slot holds amax here
     const int64_t nv = n / V::EPL;
     const int64_t step = (int64_t)gridDim.x * 256 * TQ_UNROLL;
     by_path(d, [&](auto path) {
@@ -296,20 +320,21 @@ __global__ __launch_bounds__(256) void tensor_quant(const void* __restrict__ x, 
 #pragma unroll
             for (int u = 0; u < TQ_UNROLL; ++u) {
                 const int64_t idx = base + u * 256 + threadIdx.x;
-                if (idx < nv) v[u].template store<P>(q, idx, d);
+                if (idx < nv) v[u].template store<O, P>(q, idx, d);
             }
         }
         if (blockIdx.x == 0)
-            for (int64_t i = nv * V::EPL + threadIdx.x; i < n; i += 256) q[i] = e4m3_one(quot<P>(V::scalar(x, i), d));
+            for (int64_t i = nv * V::EPL + threadIdx.x; i < n; i += 256) q[i] = cast_one<O>(quot<P>(V::scalar(x, i), d));
     });
 }
 
+template <class O>
 __global__ void tensor_scale_finish(float* __restrict__ scale) {
-    if (threadIdx.x == 0) scale[0] = scale[0] / 448.0f;   // amax -> amax / 448, as each workgroup computed it
+    if (threadIdx.x == 0) scale[0] = scale[0] / O::MAX;   // amax -> amax / MAX, as each workgroup computed it
 }
 
 // ---- launchers
-template <class V>
+template <class V, class O>
 static hipError_t launch_rows(const void* x, int64_t rows, int64_t cols, uint8_t* q, float* scale, hipStream_t stream) {
     const dim3 block(256);
     const int64_t wave_blocks = (rows + QROWS_PER_BLOCK - 1) / QROWS_PER_BLOCK;
@@ -317,21 +342,21 @@ static hipError_t launch_rows(const void* x, int64_t rows, int64_t cols, uint8_t
     const dim3 gw((unsigned)wave_blocks), gr((unsigned)rows);
     if (cols % V::EPL == 0) {
         const int64_t nv = cols / V::EPL;   // 16-byte loads per row
-        if (nv <= 64) quantize_rows_wave<V, 1><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 128) quantize_rows_wave<V, 2><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 256) quantize_rows_wave<V, 4><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 512) quantize_rows_wg<V, 2><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 1024) quantize_rows_wg<V, 4><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 2048) quantize_rows_wg<V, 8><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
-        else if (nv <= 4096) quantize_rows_wg<V, 16><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
-        else quantize_rows_wg<V, 0><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
+        if (nv <= 64) quantize_rows_wave<V, O, 1><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 128) quantize_rows_wave<V, O, 2><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 256) quantize_rows_wave<V, O, 4><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 512) quantize_rows_wg<V, O, 2><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 1024) quantize_rows_wg<V, O, 4><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 2048) quantize_rows_wg<V, O, 8><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
+        else if (nv <= 4096) quantize_rows_wg<V, O, 16><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
+        else quantize_rows_wg<V, O, 0><<<gr, block, 0, stream>>>(x, rows, cols, q, scale);
     } else {
-        quantize_rows_scalar<V><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
+        quantize_rows_scalar<V, O><<<gw, block, 0, stream>>>(x, rows, cols, q, scale);
     }
     return hipGetLastError();
 }
 
-template <class V>
+template <class V, class O>
 static hipError_t launch_tensor(const void* x, int64_t n, uint8_t* q, float* scale, hipStream_t stream) {
     const int64_t nv = n / V::EPL;
     int64_t blocks = (nv + 256 * TQ_UNROLL - 1) / (256 * TQ_UNROLL);
@@ -340,23 +365,30 @@ static hipError_t launch_tensor(const void* x, int64_t n, uint8_t* q, float* sca
     const dim3 grid((unsigned)blocks), block(256);
     tensor_scale_clear<<<1, 64, 0, stream>>>(scale);
     tensor_amax<V><<<grid, block, 0, stream>>>(x, n, scale);
-    tensor_quant<V><<<grid, block, 0, stream>>>(x, n, q, scale);
-    tensor_scale_finish<<<1, 64, 0, stream>>>(scale);
+    tensor_quant<V, O><<<grid, block, 0, stream>>>(x, n, q, scale);
+    tensor_scale_finish<O><<<1, 64, 0, stream>>>(scale);
     return hipGetLastError();
+}
+
+template <class O>
+static hipError_t launch_fmt(const void* x, int in_bf16, int64_t rows, int64_t cols, int per_tensor, uint8_t* q,
+                             float* scale, hipStream_t stream) {
+    if (per_tensor)
+        return in_bf16 ? launch_tensor<InBF16, O>(x, rows * cols, q, scale, stream)
+                       : launch_tensor<InF32, O>(x, rows * cols, q, scale, stream);
+    return in_bf16 ? launch_rows<InBF16, O>(x, rows, cols, q, scale, stream)
+                   : launch_rows<InF32, O>(x, rows, cols, q, scale, stream);
 }
 
 hipError_t launch_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                                    hipStream_t stream) {
-    return launch_rows<InF32>(x, rows, cols, q, scale, stream);
+    return launch_rows<InF32, OutE4M3>(x, rows, cols, q, scale, stream);
 }
 
-hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t cols, int per_tensor, uint8_t* q,
-                           float* scale, hipStream_t stream) {
-    if (per_tensor)
-        return in_bf16 ? launch_tensor<InBF16>(x, rows * cols, q, scale, stream)
-                       : launch_tensor<InF32>(x, rows * cols, q, scale, stream);
-    return in_bf16 ? launch_rows<InBF16>(x, rows, cols, q, scale, stream)
-                   : launch_rows<InF32>(x, rows, cols, q, scale, stream);
+hipError_t launch_quantize(const void* x, int in_bf16, int64_t rows, int64_t cols, int per_tensor, int out_e5m2,
+                           uint8_t* q, float* scale, hipStream_t stream) {
+    return out_e5m2 ? launch_fmt<OutE5M2>(x, in_bf16, rows, cols, per_tensor, q, scale, stream)
+                    : launch_fmt<OutE4M3>(x, in_bf16, rows, cols, per_tensor, q, scale, stream);
 }
 
 }  // namespace fp8g

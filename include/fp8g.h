@@ -6,7 +6,7 @@
  * Operations (definitions in each entry point's comment):
  *   fp8_quantize_rowwise  fp32 [rows, cols] -> E4M3 codes + one fp32 scale per row
  *   fp8_quantize_ex       the same quantizer for fp32 or bf16 input, with one
- *                         scale per row or one per tensor
+ *                         scale per row or one per tensor, to E4M3 or E5M2
  *   mxfp8_quantize        fp32 [rows, cols] -> E4M3 codes + one UE8M0 scale per
  *                         32 consecutive elements of a row (MXFP8)
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
@@ -20,7 +20,7 @@
  * Common conventions
  *   - Every array is dense and row-major; the caller owns all memory.  A is
  *     [m, k] and B is [n, k], both with k contiguous ("K-major"); D is
- *     [m, n] with n contiguous.  E4M3 operands are passed as their byte codes.
+ *     [m, n] with n contiguous.  FP8 operands are passed as their byte codes.
  *   - Device pointers must stay valid until the work queued on `stream`
  *     has run.  `stream` may be 0 (the null stream).
  *   - Every pointer must be 16-byte aligned (else FP8G_ERR_ALIGN), except
@@ -29,7 +29,9 @@
  *     returns its status and queues nothing.  A launch failure returns
  *     FP8G_ERR_HIP.  Faults inside a kernel surface at the caller's next
  *     synchronization, as with any HIP kernel.
- *   - Results are bitwise reproducible run to run (no atomics, fixed order).
+ *   - Results are bitwise reproducible run to run: sums run in a fixed
+ *     order; the one atomic (the per-tensor amax) is a max, which no order
+ *     changes.
  *   - Calls are thread-safe: the library keeps no mutable state.
  */
 #ifndef FP8G_H
@@ -129,8 +131,9 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
                     void* D, int out_dtype, hipStream_t stream);
 
 /*
- * fp8_quantize_ex -- E4M3 quantization with the scale rule of
- * fp8_quantize_rowwise, for fp32 or bf16 input, per row or per tensor.
+ * fp8_quantize_ex -- FP8 quantization with the scale rule of
+ * fp8_quantize_rowwise, for fp32 or bf16 input, per row or per tensor, to E4M3
+ * or E5M2 codes.
  *
  * Source: the scale rule abs_max / 448 in `_calibrate_scales` of the
  * hybrid-inference class on the page "FP8 推理基础设施（五）：从 DeepGEMM 到
@@ -138,24 +141,31 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
  * fp8_quantize_rowwise.  bf16 is the precision models are usually deployed in
  * (page on FP8 vLLM for AMD Instinct, introduction); each bf16 value is
  * converted to fp32 exactly (its bits shifted up by 16), so the result is that
- * of the fp32 quantizer on the converted tensor.
+ * of the fp32 quantizer on the converted tensor.  E5M2 output (the page on
+ * FlashInfer's concat_mla_k with FP8 inputs takes E5M2 beside E4M3) uses the
+ * same rule with that format's largest finite value: MAX = 448 (E4M3) or
+ * 57344 (E5M2).
  *
- *   per row:    s[r] = fp32(max_c |x[r,c]| / 448),  q[r,c] = E4M3_RNE_SAT(fp32(x[r,c] / s[r]))
- *   per tensor: s[0] = fp32(max_{r,c} |x[r,c]| / 448), q[r,c] = E4M3_RNE_SAT(fp32(x[r,c] / s[0]))
- *   a zero scale gives signed zeros, as in fp8_quantize_rowwise.
+ *   per row:    s[r] = fp32(max_c |x[r,c]| / MAX),  q[r,c] = RNE_SAT(fp32(x[r,c] / s[r]))
+ *   per tensor: s[0] = fp32(max_{r,c} |x[r,c]| / MAX), q[r,c] = RNE_SAT(fp32(x[r,c] / s[0]))
+ *   RNE_SAT: round to nearest even in the output format, magnitudes above MAX
+ *   saturate to MAX, sign copied; a zero scale gives signed zeros, as in
+ *   fp8_quantize_rowwise.
  *
  * x        device, [rows, cols] of in_dtype (FP8G_IN_F32 / FP8G_IN_BF16), read only
- * q        device, E4M3 codes [rows, cols], written
+ * out_fmt  FP8G_FMT_E4M3 or FP8G_FMT_E5M2
+ * q        device, codes of out_fmt [rows, cols], written
  * scale    device, fp32, written: [rows] (FP8G_SCALE_PER_ROW) or [1]
  *          (FP8G_SCALE_PER_TENSOR; it holds an intermediate until the call's
  *          work on the stream has finished)
  * rows, cols >= 0.  Per row: rows == 0 is a no-op.  Per tensor: the scale is
  * always written (0 for an empty tensor).  Bit-exact with the definition.
- * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_DTYPE (unknown in_dtype or
- * granularity), ERR_ALIGN, ERR_OVERLAP, ERR_UNSUPPORTED (size overflow), ERR_HIP.
+ * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_DTYPE (unknown in_dtype,
+ * granularity or out_fmt), ERR_ALIGN, ERR_OVERLAP, ERR_UNSUPPORTED (size
+ * overflow), ERR_HIP.
  */
 int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int granularity,
-                    uint8_t* q, float* scale, hipStream_t stream);
+                    int out_fmt, uint8_t* q, float* scale, hipStream_t stream);
 
 /*
  * mxfp8_quantize -- MXFP8 block quantization (the step before mxfp8_gemm).

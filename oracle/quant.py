@@ -18,6 +18,12 @@ Readings taken where the pages are silent (listed in the design notes):
   * if s == 0 (all-zero or empty row, or amax so tiny that amax/448
     underflows), s is written as 0 and every code is a zero with x's sign.
 
+E5M2 output (``fmt="e5m2"``): the same rule with that format's largest
+finite value, 57344, in place of 448, and the saturating round-to-nearest-even
+E5M2 cast (oracle.e5m2).  The pages take E5M2 beside E4M3 (page on
+FlashInfer's concat_mla_k with FP8 inputs, sections 1-2) but state no scale
+rule for it; this is the plainest reading of the E4M3 rule for it.
+
 ``mx_quantize``: the MXFP8 block quantizer that builds mode-(b) inputs.  One
 unsigned 8-bit power-of-two scale per 32 consecutive K elements of each row
 (scale tensor shape ``(n, k // 32)`` and ``num_elts_per_sf=32`` on the page
@@ -29,33 +35,36 @@ clamped to [-127, 127]; an all-zero block takes e = -127.
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
+_FORMATS = {"e4m3": (e4m3, E4M3_MAX), "e5m2": (e5m2, E5M2_MAX)}
 MX_BLOCK = 32
 UE8M0_BIAS = 127
 
 
-def row_scales(x) -> np.ndarray:
-    """s[r] = fp32(max_c |x[r,c]| / 448); empty rows give 0."""
+def row_scales(x, fmt="e4m3") -> np.ndarray:
+    """s[r] = fp32(max_c |x[r,c]| / MAX) (MAX = 448 for E4M3, 57344 for E5M2);
+    empty rows give 0."""
     x = np.asarray(x, dtype=np.float32)
     if x.shape[1] == 0:
         return np.zeros(x.shape[0], dtype=np.float32)
     amax = np.max(np.abs(x), axis=1)               # exact: a max does not round
-    return (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return (amax / np.float32(_FORMATS[fmt][1])).astype(np.float32)
 
 
-def quantize_rowwise(x):
-    """Per-row E4M3 quantization: returns (codes uint8 [R,C], scales fp32 [R])."""
+def quantize_rowwise(x, fmt="e4m3"):
+    """Per-row quantization to E4M3 (or E5M2): returns (codes uint8 [R,C], scales fp32 [R])."""
     x = np.asarray(x, dtype=np.float32)
     if x.ndim != 2:
         raise ValueError("quantize_rowwise expects a 2-D array")
-    s = row_scales(x)
+    s = row_scales(x, fmt)
     zero_row = s == 0
     safe = np.where(zero_row, np.float32(1.0), s).astype(np.float32)
     y = (x / safe[:, None]).astype(np.float32)     # IEEE fp32 divide, round to nearest
     y = np.where(zero_row[:, None], np.copysign(np.float32(0.0), x), y).astype(np.float32)
-    return e4m3.encode(y), s
+    return _FORMATS[fmt][0].encode(y), s
 
 
 def bf16_to_f32(bits) -> np.ndarray:
@@ -65,18 +74,18 @@ def bf16_to_f32(bits) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def quantize_tensorwise(x):
-    """Per-tensor E4M3 quantization: one scale for the whole tensor, the
-    amax/448 of `_calibrate_scales` on the DeepGEMM page (abs_max over the data).
-    Returns (codes uint8 [same shape], scale fp32 [1])."""
+def quantize_tensorwise(x, fmt="e4m3"):
+    """Per-tensor quantization: one scale for the whole tensor, the amax/448 of
+    `_calibrate_scales` on the DeepGEMM page (abs_max over the data; amax/57344
+    for E5M2).  Returns (codes uint8 [same shape], scale fp32 [1])."""
     x = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
-    s = np.float32(amax / np.float32(E4M3_MAX))               # IEEE fp32 divide
+    s = np.float32(amax / np.float32(_FORMATS[fmt][1]))       # IEEE fp32 divide
     if s == 0:
         y = np.copysign(np.float32(0.0), x).astype(np.float32)
     else:
         y = (x / s).astype(np.float32)                        # IEEE fp32 divide, round to nearest
-    return e4m3.encode(y), np.array([s], dtype=np.float32)
+    return _FORMATS[fmt][0].encode(y), np.array([s], dtype=np.float32)
 
 
 def mx_block_exponent(amax) -> np.ndarray:

@@ -124,8 +124,8 @@ def test_quantize_argument_checks(lib):
     assert quant(lib, cols=0, x=None, q=None) in (OK, HIP)    # empty rows: only scales written
 
 
-def qex(lib, x=P_(0), dt=0, rows=8, cols=64, g=0, q=P_(1 << 30), s=P_(2 << 30)):
-    return lib.fp8_quantize_ex(x, dt, rows, cols, g, q, s, ctypes.c_void_p(S))
+def qex(lib, x=P_(0), dt=0, rows=8, cols=64, g=0, q=P_(1 << 30), s=P_(2 << 30), fmt=1):
+    return lib.fp8_quantize_ex(x, dt, rows, cols, g, fmt, q, s, ctypes.c_void_p(S))
 
 
 def test_quantize_ex_argument_checks(lib):
@@ -141,6 +141,9 @@ def test_quantize_ex_argument_checks(lib):
     assert qex(lib, dt=2) == DTYPE
     assert qex(lib, dt=-1) == DTYPE
     assert qex(lib, g=2) == DTYPE
+    assert qex(lib, fmt=2) == DTYPE
+    assert qex(lib, fmt=-1) == DTYPE
+    assert qex(lib, fmt=0, s=None) == NULL and qex(lib, fmt=1, s=None) == NULL   # both formats accepted
     assert qex(lib, rows=0, x=None, q=None, s=None) == OK                # per row, empty: no-op
     assert qex(lib, rows=0, x=None, q=None, s=None, g=1) == NULL         # per tensor: the scale is written
     assert qex(lib, rows=0, x=None, q=None, g=1) in (OK, HIP)

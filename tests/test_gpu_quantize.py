@@ -1,4 +1,5 @@
-"""GPU parity of fp8_quantize_rowwise: bit-exact codes and scales vs the oracle."""
+"""GPU parity of fp8_quantize_rowwise and fp8_quantize_ex (bf16 input, one
+scale per tensor, E5M2 output): bit-exact codes and scales vs the oracle."""
 
 import os
 
@@ -253,3 +254,114 @@ def test_quantize_ex_fp32_rows_equal_rowwise(gpu_lib):
     q1, s1 = gpu_lib.fp8_quantize_rowwise(x)
     q2, s2 = gpu_lib.fp8_quantize_ex(x)
     assert np.array_equal(to_host(q1), to_host(q2)) and np.array_equal(to_host(s1), to_host(s2))
+
+
+# ---- E5M2 output (fp8_quantize_ex with fmt = E5M2): scale amax / 57344
+
+E5M2 = 1
+
+
+def check_ex(fp8g, x, what, per_tensor=False, bf16=False):
+    """fp8_quantize_ex to E5M2 vs the oracle on the same (bf16-converted) values."""
+    say("quantize e5m2", what, x.shape, "per tensor" if per_tensor else "per row", "bf16" if bf16 else "f32")
+    if bf16:
+        bits = _bf16_bits(x)
+        xin, x32 = _dev_bf16(bits), quant.bf16_to_f32(bits)
+    else:
+        xin, x32 = to_dev(x), x
+    q, s = fp8g.fp8_quantize_ex(xin, per_tensor=per_tensor, fmt=E5M2)
+    import torch
+    assert q.dtype == torch.float8_e5m2
+    qg, sg = q.view(torch.uint8).cpu().numpy(), to_host(s)
+    if per_tensor:
+        qr, sr = quant.quantize_tensorwise(x32, "e5m2")
+    else:
+        qr, sr = quant.quantize_rowwise(x32, "e5m2")
+    assert np.array_equal(sg.view(np.uint32), sr.view(np.uint32)), what + ": scales differ"
+    if not np.array_equal(qg, qr):
+        r, c = np.argwhere(qg != qr)[0]
+        raise AssertionError("%s: %d codes differ; first at (%d,%d): x=%r gpu=%02x oracle=%02x"
+                             % (what, int((qg != qr).sum()), r, c, x32[r, c], qg[r, c], qr[r, c]))
+
+
+E5M2_SHAPES = [(1, 4), (5, 60), (9, 260), (128, 512), (6, 1000), (33, 4096), (130, 8192), (4, 10000),
+               (5, 257), (3, 3), (3, 16384), (2, 40000)]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("rows,cols", E5M2_SHAPES)
+def test_quantize_e5m2_rows(gpu_lib, rows, cols, bf16):
+    w = synth.Workload("q5", rows, rows, cols, "a", "rowfactor_outlier", "normal", "rowwise", 29)
+    check_ex(gpu_lib, synth.draw(w, "a"), "rowfactor_outlier", bf16=bf16)
+
+
+def e5m2_edge_rows(cols=64):
+    t = 2.0 ** -149
+    rows = [
+        np.zeros(cols),
+        np.where(np.arange(cols) % 2 == 0, 0.0, -0.0),
+        np.r_[t, -t, np.zeros(cols - 2)],                            # amax/57344 underflows: s = 0
+        np.r_[2 ** 20 * t, 300 * t, -(2 ** 20) * t, np.zeros(cols - 3)],   # subnormal s
+        np.r_[114688.0, 1.0, -3.0, 0.5, 2.0 ** -15, 3 * 2.0 ** -16, -2.0 ** -20, np.zeros(cols - 7)],
+        np.linspace(-57344, 57344, cols),                            # s = 1: plain cast
+        np.r_[57344.0, (np.arange(1, cols) + 0.5) * 2.0 ** -16],     # subnormal midpoints at s = 1
+        np.full(cols, 3.0e38),
+        np.r_[2.0 ** 100, 2.0 ** 70, -1.0, np.zeros(cols - 3)],
+    ]
+    return np.array(rows, dtype=np.float32)
+
+
+@pytest.mark.parametrize("cols", [64, 67])
+def test_quantize_e5m2_edge_rows(gpu_lib, cols):
+    check_ex(gpu_lib, e5m2_edge_rows(cols), "e5m2 edge rows, cols=%d" % cols)
+    check_ex(gpu_lib, edge_rows(cols), "e4m3 edge rows as e5m2, cols=%d" % cols)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_e5m2_per_tensor(gpu_lib, bf16):
+    for name, x in _tensor_cases():
+        check_ex(gpu_lib, x, name, per_tensor=True, bf16=bf16)
+
+
+def test_quantize_e5m2_division_near_rounding_boundaries(gpu_lib):
+    """Quotients within 3 fp32 ulps of every E5M2 rounding boundary (the
+    midpoints between adjacent magnitudes), both signs, over 2048 log-uniform
+    row scales and scales with all-ones or unit significands."""
+    from oracle import e5m2
+    mags = e5m2.DECODE_TABLE[:0x7C]
+    thr = (mags[:-1] + mags[1:]) / 2                                    # 123 boundaries, exact in fp32
+    u = synth.uniform(synth.stream_key(0x5EED, 2), 0, 2048)
+    s0 = np.concatenate([np.exp2(40.0 * u - 20.0), np.ldexp(2.0 - 2.0 ** -23, np.arange(-20, 20)),
+                         np.ldexp(1.0, np.arange(-20, 20))])
+    amax = (57344.0 * s0).astype(np.float32)
+    s = amax / np.float32(57344.0)
+    cols = 7 * 2 * thr.size + 1
+    x = np.zeros((len(s0), cols), np.float32)
+    x[:, 0] = amax
+    base = (thr[None, :] * s.astype(np.float64)[:, None]).astype(np.float32)
+    c = 1
+    for k in range(-3, 4):
+        v = base.copy()
+        for _ in range(abs(k)):
+            v = np.nextafter(v, np.float32(np.inf) if k > 0 else np.float32(0.0))
+        for sign in (1.0, -1.0):
+            x[:, c:c + thr.size] = np.float32(sign) * v
+            c += thr.size
+    check_ex(gpu_lib, x, "e5m2 division near rounding boundaries")
+
+
+def test_quantize_e5m2_feeds_e5m2_gemm(gpu_lib):
+    """GPU E5M2 quantizer -> GPU GEMM with E5M2 activations and E4M3 weights ==
+    oracle quantizers -> oracle GEMM within the GEMM bound."""
+    from gpu_util import assert_gemm_close
+    from oracle import gemm
+    w = synth.Workload("q5g", 300, 260, 1024, "a", "rowfactor_outlier", "normal", "rowwise", 31)
+    XA, XB = synth.draw(w, "a"), synth.draw(w, "b")
+    qa, sa = gpu_lib.fp8_quantize_ex(to_dev(XA), fmt=E5M2)
+    qb, sb = gpu_lib.fp8_quantize_rowwise(to_dev(XB))
+    D = to_host(gpu_lib.fp8_gemm_scaled_ex(w.M, w.N, w.K, qa, E5M2, qb, 0, sa, sb))
+    oa, osa = quant.quantize_rowwise(XA, "e5m2")
+    ob, osb = quant.quantize_rowwise(XB)
+    assert_gemm_close(D, gemm.gemm_scaled(oa, ob, osa, osb, "e5m2", "e4m3"),
+                      gemm.gemm_scaled_weight(oa, ob, osa, osb, "e5m2", "e4m3"), "bf16", "e5m2 quantize -> gemm",
+                      gemm.alignment_term(oa, ob, osa, osb, fmt_a="e5m2", fmt_b="e4m3"))

@@ -191,3 +191,60 @@ def test_tensorwise_zero_and_empty():
     assert s.tolist() == [0.0] and q.tolist() == [[0x00, 0x80]]
     q, s = quant.quantize_tensorwise(np.zeros((0, 5), np.float32))
     assert s.tolist() == [0.0] and q.shape == (0, 5)
+
+
+# ---------------------------------------------------------------- E5M2 output
+# Expected codes below are worked from the E5M2 bit definition (value =
+# (4+m) * 2^(e-17), subnormals m * 2^-16), not from the oracle's encoder.
+
+from oracle import e5m2  # noqa: E402
+
+
+def test_e5m2_power_of_two_scale_row():
+    # amax 114688 -> s = 114688 / 57344 = 2 exactly; codes are those of x / 2
+    x = np.array([[114688.0, 1.0, -3.0, 0.5, 2.0 ** -15, 3 * 2.0 ** -16, -2.0 ** -20, 0.0]], dtype=np.float32)
+    q, s = quant.quantize_rowwise(x, "e5m2")
+    assert s[0] == 2.0
+    # x/2 = 57344, 0.5, -1.5, 0.25, 2^-16, 1.5*2^-16 (tie between subnormal codes 1 and 2 -> even),
+    # -2^-21 (-> -0), 0
+    assert list(q[0]) == [0x7B, 0x38, 0xBE, 0x34, 0x01, 0x02, 0x80, 0x00]
+
+
+def test_e5m2_unit_scale_row_is_plain_cast():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4, 300)).astype(np.float32) * 3000
+    x[:, 0] = -57344.0
+    q, s = quant.quantize_rowwise(x, "e5m2")
+    assert np.all(s == 1.0)
+    import torch
+    assert np.array_equal(q, torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy())
+
+
+def test_e5m2_amax_element_maps_to_max_and_error_bound():
+    x = _rows_of_all_kinds()
+    q, s = quant.quantize_rowwise(x, "e5m2")
+    normal = s >= np.float32(2.0 ** -126)
+    assert normal.sum() >= x.shape[0] - 1
+    for r in np.nonzero(normal)[0]:
+        j = np.argmax(np.abs(x[r]))
+        assert q[r, j] & 0x7F == 0x7B and (q[r, j] >> 7) == np.signbit(x[r, j])
+    # |dec(q) s - x| <= (2^-3 + 2^-22)|x| + 2^-17 s: half an E5M2 step (2 mantissa bits), the fp32
+    # division, and half the subnormal step
+    d = e5m2.decode(q[normal]) * s[normal].astype(np.float64)[:, None]
+    xn = x[normal].astype(np.float64)
+    bound = (2.0 ** -3 + 2.0 ** -22) * np.abs(xn) + 2.0 ** -17 * s[normal].astype(np.float64)[:, None]
+    err = np.abs(d - xn)
+    assert np.all(err <= bound) and np.max(err / bound) > 0.3
+    # E5M2 keeps less precision than E4M3 on the same rows
+    q4, s4 = quant.quantize_rowwise(x[normal])
+    err4 = np.abs(e4m3.decode(q4) * s4.astype(np.float64)[:, None] - xn)
+    assert err.sum() > err4.sum()
+
+
+def test_e5m2_tensorwise_is_rowwise_of_the_flattened_tensor():
+    w = synth.WORKLOADS["c2_2048x1024x4096"]
+    x = synth.draw(w, "a", slice(0, 16))[:, :500].copy()
+    q, s = quant.quantize_tensorwise(x, "e5m2")
+    q1, s1 = quant.quantize_rowwise(x.reshape(1, -1), "e5m2")
+    assert np.array_equal(q.reshape(1, -1), q1) and s[0] == s1[0]
+    assert s[0] == np.float32(np.float32(np.abs(x).max()) / np.float32(57344.0))
