@@ -1,6 +1,7 @@
 """Benchmark of the FP8 scaled-GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--fmt-a e4m3|e5m2] [--fmt-b e4m3|e5m2]
 
 One step = one pass of the whole path over one batch of seeded synthetic
 input already resident in HBM:
@@ -8,6 +9,8 @@ input already resident in HBM:
       fp8_quantize_rowwise(X_A) -> A, sa      (activations, per token)
       fp8_quantize_rowwise(X_B) -> B, sb      (weights, per output channel)
       fp8_gemm_scaled(A, B, sa, sb) -> D      (bf16)
+      with --fmt-a / --fmt-b e5m2: fp8_quantize_ex(X, fmt) to that operand's
+      format and fp8_gemm_scaled_ex (default: both E4M3)
   mx (4096 x 14336 x 4096, MXFP8):
       mxfp8_quantize(X_A) -> A, ea            (UE8M0 per 32 K elements)
       mxfp8_quantize(X_B) -> B, eb
@@ -55,6 +58,10 @@ def parse():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up",
                    help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fmt-a", choices=["e4m3", "e5m2"], default="e4m3",
+                   help="ffn_up: format of the activation operand A")
+    p.add_argument("--fmt-b", choices=["e4m3", "e5m2"], default="e4m3",
+                   help="ffn_up: format of the weight operand B")
     p.add_argument("--traffic", default=None,
                    help="counter summary with the measured HBM bytes per GEMM launch (default: the one "
                         "under profiles/ for the workload)")
@@ -77,7 +84,7 @@ def copy_only(nbytes, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "seconds": dt, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
 
 
-def cpu_baseline_ffn_up(w, m_s=4096, n_s=16384):
+def cpu_baseline_ffn_up(w, m_s=4096, n_s=16384, fa="e4m3", fb="e4m3"):
     """The oracle on a sample: rows 0..m_s of the activations, rows 0..n_s of the
     weights: quantize both (row-wise) and form the m_s x n_s block of D."""
     from oracle import gemm, quant
@@ -89,10 +96,10 @@ def cpu_baseline_ffn_up(w, m_s=4096, n_s=16384):
     sa = np.empty(m_s, np.float32)
     sb = np.empty(n_s, np.float32)
     for r in range(0, m_s, 256):
-        qa[r:r + 256], sa[r:r + 256] = quant.quantize_rowwise(XA[r:r + 256])
+        qa[r:r + 256], sa[r:r + 256] = quant.quantize_rowwise(XA[r:r + 256], fa)
     for r in range(0, n_s, 256):
-        qb[r:r + 256], sb[r:r + 256] = quant.quantize_rowwise(XB[r:r + 256])
-    gemm.gemm_scaled(qa, qb, sa, sb)
+        qb[r:r + 256], sb[r:r + 256] = quant.quantize_rowwise(XB[r:r + 256], fb)
+    gemm.gemm_scaled(qa, qb, sa, sb, fa, fb)
     dt = time.perf_counter() - t0
     flops = 2.0 * m_s * n_s * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
@@ -228,6 +235,10 @@ def main():
         copy_only(args.copy_bytes)
         return
     fp8g.load()
+    e4m3_only = args.fmt_a == "e4m3" and args.fmt_b == "e4m3"
+    if not e4m3_only and args.workload != "ffn_up":
+        print("--fmt-a / --fmt-b apply to the ffn_up workload only", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "concat_mla":
         concat_bench(args, torch, fp8g)
         return
@@ -247,16 +258,28 @@ def main():
         sa = torch.empty((M,), dtype=torch.float32, device=dev)
         sb = torch.empty((N,), dtype=torch.float32, device=dev)
 
+        fa = fp8g.FMT_E5M2 if args.fmt_a == "e5m2" else fp8g.FMT_E4M3
+        fb = fp8g.FMT_E5M2 if args.fmt_b == "e5m2" else fp8g.FMT_E4M3
+
         def step(ev=None):
             if ev is not None:
                 ev[0].record(stream)
-            fp8g.fp8_quantize_rowwise(XA, qa, sa)
+            if e4m3_only:
+                fp8g.fp8_quantize_rowwise(XA, qa, sa)
+            else:
+                fp8g.fp8_quantize_ex(XA, q=qa, scale=sa, fmt=fa)
             if ev is not None:
                 ev[1].record(stream)
-            fp8g.fp8_quantize_rowwise(XB, qb, sb)
+            if e4m3_only:
+                fp8g.fp8_quantize_rowwise(XB, qb, sb)
+            else:
+                fp8g.fp8_quantize_ex(XB, q=qb, scale=sb, fmt=fb)
             if ev is not None:
                 ev[2].record(stream)
-            fp8g.fp8_gemm_scaled(M, N, K, qa, qb, sa, sb, D=D)
+            if e4m3_only:
+                fp8g.fp8_gemm_scaled(M, N, K, qa, qb, sa, sb, D=D)
+            else:
+                fp8g.fp8_gemm_scaled_ex(M, N, K, qa, fa, qb, fb, sa, sb, D=D)
             if ev is not None:
                 ev[3].record(stream)
         kernels = ["quantize_activations", "quantize_weights", "gemm"]
@@ -300,7 +323,8 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_us = per_kernel["gemm"]
     achieved = flops / (gemm_us * 1e-6) / 1e12
-    traffic = read_traffic(args.traffic or os.path.join(ROOT, TRAFFIC_FILES[args.workload]))
+    # the counter summary covers the E4M3 x E4M3 kernel only
+    traffic = read_traffic(args.traffic or os.path.join(ROOT, TRAFFIC_FILES[args.workload])) if e4m3_only else None
     line = {
         "metric": "FP8 GEMM TFLOP/s and % of FP8 MFMA peak at MxNxK=8192x22016x8192"
                   if args.workload == "ffn_up" else "MXFP8 GEMM TFLOP/s at 4096x14336x4096",
@@ -313,11 +337,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3",
+        "dtype": "fp8_e4m3" if e4m3_only else "fp8_%s x fp8_%s" % (args.fmt_a, args.fmt_b),
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "out": "bf16",
                    "mode": "per-token x per-channel scales" if w.mode == "a" else "MXFP8",
-                   "step": " -> ".join(kernels)},
+                   "step": " -> ".join(kernels), "fmt_a": args.fmt_a, "fmt_b": args.fmt_b},
         "pct_of_fp8_peak_step": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
@@ -331,7 +355,8 @@ def main():
     line["quantizer_gbs"] = {k: round(b / (per_kernel[k] * 1e-6) / 1e9, 1) for k, b in qbytes.items()}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline_ffn_up(w) if w.mode == "a" else cpu_baseline_mx(w)
+        line["cpu_baseline"] = (cpu_baseline_ffn_up(w, fa=args.fmt_a, fb=args.fmt_b) if w.mode == "a"
+                                else cpu_baseline_mx(w))
     print(json.dumps(line), flush=True)
 
 
