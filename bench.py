@@ -126,20 +126,23 @@ def cpu_baseline_mx(w, m_s=2048, n_s=8192):
 
 
 TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic.txt",
-                 "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt"}
+                 "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt",
+                 "concat_mla": "profiles/concat_mla_k_fp8_16384x128_hbm_traffic.txt"}
+KERNEL_SOURCES = {"ffn_up": "gemm.hip", "mx": "gemm.hip", "concat_mla": "concat.hip"}
 
 
-def source_digest():
-    """sha256 of the GEMM kernel source: counters taken on another version of it
+def source_digest(name="gemm.hip"):
+    """sha256 of a kernel source file: counters taken on another version of it
     do not describe the kernel being timed."""
     import hashlib
-    with open(os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", "gemm.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_traffic(path):
-    """HBM bytes per GEMM launch from a counter summary ('key: value' lines), or
-    None when the file is missing or was taken on a different kernel source."""
+def read_traffic(path, source="gemm.hip"):
+    """HBM bytes per launch of the dominant kernel from a counter summary
+    ('key: value' lines), or None when the file is missing or was taken on a
+    different version of the kernel's source file."""
     if not path or not os.path.exists(path):
         return None
     kv = {}
@@ -147,7 +150,7 @@ def read_traffic(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_digest():
+    if kv.get("source_sha256") != source_digest(source):
         log("traffic summary %s was taken on another kernel source: traffic = null" % path)
         return None
     try:
@@ -201,7 +204,8 @@ def concat_bench(args, torch, fp8g):
                        "elem_bytes": 1, "rope_heads": 1},
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": None, "kernel": "concat_mla_k_kernel", "bytes_per_launch": nbytes}}
+                         "traffic": read_traffic(os.path.join(ROOT, TRAFFIC_FILES["concat_mla"]), "concat.hip"),
+                         "kernel": "concat_mla_k_kernel", "bytes_per_launch": nbytes}}
     if not args.no_cpu_baseline:
         from oracle import concat
         ts = 2048                                            # tokens in the sample
