@@ -42,7 +42,7 @@ import synth  # noqa: E402
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 WORKLOADS = {"ffn_up": "c4_ffn_up_8192x22016x8192", "mx": "c5_mx_4096x14336x4096",
-             "concat_mla": "concat_mla_k_fp8_16384x128"}
+             "concat_mla": "concat_mla_k_fp8_16384x128", "quantize": "c4_ffn_up_8192x22016x8192"}
 CONCAT_T, CONCAT_H = 16384, 128     # tokens x heads, 1-byte elements, rope shared by a token's heads
 
 
@@ -56,7 +56,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up",
-                   help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k")
+                   help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k; "
+                        "quantize: every fp8_quantize_ex mode on the FFN-up activations")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fmt-a", choices=["e4m3", "e5m2"], default="e4m3",
                    help="ffn_up: format of the activation operand A")
@@ -224,6 +225,74 @@ def concat_bench(args, torch, fp8g):
     print(json.dumps(line), flush=True)
 
 
+QUANT_MODES = [  # (name, bf16 input, per tensor, output format)
+    ("f32_row_e4m3", False, False, 0), ("bf16_row_e4m3", True, False, 0), ("f32_tensor_e4m3", False, True, 0),
+    ("bf16_tensor_e4m3", True, True, 0), ("f32_row_e5m2", False, False, 1), ("bf16_row_e5m2", True, False, 1)]
+
+
+def quantize_bench(args, torch, fp8g):
+    """fp8_quantize_ex on the 8192 x 8192 FFN-up activations, every mode; the
+    headline value is the fp32 row-wise E4M3 quantizer.  GB/s of algorithmic
+    bytes: the input read (4 or 2 bytes per element), the codes written (1),
+    the scales written (4 per row or 4)."""
+    w = synth.WORKLOADS[WORKLOADS["quantize"]]
+    dev = torch.device("cuda", 0)
+    X = torch.from_numpy(synth.draw(w, "a")).to(dev)
+    Xb = X.to(torch.bfloat16)
+    R, C = X.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    s_row = torch.empty((R,), dtype=torch.float32, device=dev)
+    s_ten = torch.empty((1,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, bf, pt, fmt in QUANT_MODES:
+        x = Xb if bf else X
+        sc = s_ten if pt else s_row
+
+        def call():
+            fp8g.fp8_quantize_ex(x, per_tensor=pt, q=q, scale=sc, fmt=fmt)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        nbytes = R * C * ((2 if bf else 4) + 1) + (4 if pt else 4 * R)
+        res[name] = {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes,
+                     "ms_per_call": elapsed / args.steps * 1e3}
+    head = res["f32_row_e4m3"]
+    line = {"metric": "fp8_quantize_ex GB/s on 8192x8192 activations (fp32 in, one scale per row, E4M3 out)",
+            "value": round(head["bytes"] / (head["ms_per_call"] * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_call"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "quantize_ffn_up_activations_8192x8192", "rows": R, "cols": C},
+            "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(head["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "quantize_rows_wg", "bytes_per_launch": head["bytes"]},
+            "modes": {k: {"us": v["us"], "gbs": v["gbs"], "frac": round(v["gbs"] / PEAK_HBM_GBS, 4)}
+                      for k, v in res.items()}}
+    if not args.no_cpu_baseline:
+        from oracle import quant
+        xs = X[:512].cpu().numpy()
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < 10.0:
+            quant.quantize_rowwise(xs)
+            reps += 1
+        dt = (time.perf_counter() - t1) / reps
+        line["cpu_baseline"] = {"value": round(xs.size * 5 / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "seconds": round(dt * reps, 2),
+                                "sample": "oracle quantize_rowwise (numpy) on the first 512 rows, repeated %d times"
+                                          % reps}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +314,9 @@ def main():
         sys.exit(2)
     if args.workload == "concat_mla":
         concat_bench(args, torch, fp8g)
+        return
+    if args.workload == "quantize":
+        quantize_bench(args, torch, fp8g)
         return
     w = synth.WORKLOADS[WORKLOADS[args.workload]]
     dev = torch.device("cuda", 0)
