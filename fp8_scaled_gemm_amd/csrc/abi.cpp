@@ -33,6 +33,9 @@ int64_t mul3(int64_t a, int64_t b, int64_t c) {
     return ab * c;
 }
 
+constexpr int64_t GEMM_K_LIMIT = (int64_t)1 << 23;
+constexpr int64_t ROWS_LIMIT = (int64_t)1 << 31;   // the row-wise quantizers launch one workgroup (wave) per row
+
 int check_gemm_common(int64_t m, int64_t n, int64_t k, const void* A, const void* B, const void* sa,
                       const void* sb, int64_t sa_bytes, int64_t sb_bytes, const void* D, int out_dtype) {
     if (m < 0 || n < 0 || k < 0) return FP8G_ERR_SHAPE;
@@ -41,6 +44,10 @@ int check_gemm_common(int64_t m, int64_t n, int64_t k, const void* A, const void
     const int64_t esz = out_dtype == FP8G_OUT_F32 ? 4 : 2;
     const int64_t a_bytes = mul3(m, k, 1), b_bytes = mul3(n, k, 1), d_bytes = mul3(m, n, esz);
     if (a_bytes < 0 || b_bytes < 0 || d_bytes < 0) return FP8G_ERR_UNSUPPORTED;
+    // the kernels address a 256-row panel of A, B (k bytes per row) or D (n
+    // elements per row) with 32-bit offsets below 2^31
+    if (k >= GEMM_K_LIMIT || m >= ((int64_t)1 << 31) || n * 256 * esz > ((int64_t)1 << 31))
+        return FP8G_ERR_UNSUPPORTED;
     if (!D) return FP8G_ERR_NULL;
     if (k > 0 && (!A || !B)) return FP8G_ERR_NULL;
     if (sa_bytes > 0 && !sa) return FP8G_ERR_NULL;
@@ -68,7 +75,7 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols, uint8_t* q,
     if (rows < 0 || cols < 0) return FP8G_ERR_SHAPE;
     if (rows == 0) return FP8G_OK;
     const int64_t n = mul3(rows, cols, 1);
-    if (n < 0 || n > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (n < 0 || n > ((int64_t)1 << 60) || rows >= ROWS_LIMIT) return FP8G_ERR_UNSUPPORTED;
     if (!scale) return FP8G_ERR_NULL;
     if (n > 0 && (!x || !q)) return FP8G_ERR_NULL;
     if (!aligned16(scale) || (x && !aligned16(x)) || (q && !aligned16(q))) return FP8G_ERR_ALIGN;
@@ -86,7 +93,7 @@ int fp8_quantize_ex(const void* x, int in_dtype, int64_t rows, int64_t cols, int
     const bool per_tensor = granularity == FP8G_SCALE_PER_TENSOR;
     if (!per_tensor && rows == 0) return FP8G_OK;
     const int64_t n = mul3(rows, cols, 1);
-    if (n < 0 || n > ((int64_t)1 << 60)) return FP8G_ERR_UNSUPPORTED;
+    if (n < 0 || n > ((int64_t)1 << 60) || (!per_tensor && rows >= ROWS_LIMIT)) return FP8G_ERR_UNSUPPORTED;
     if (!scale) return FP8G_ERR_NULL;
     if (n > 0 && (!x || !q)) return FP8G_ERR_NULL;
     if (!aligned16(scale) || (x && !aligned16(x)) || (q && !aligned16(q))) return FP8G_ERR_ALIGN;
@@ -165,7 +172,7 @@ const char* fp8g_status_string(int status) {
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case FP8G_ERR_DTYPE: return "unknown output dtype, input dtype, granularity or element size";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
-        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (k % 16 for fp8_gemm_scaled, or size overflow)";
+        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (GEMM: k % 16, k >= 2^23, a 256-row panel of D of 2^31 bytes or more; rows >= 2^31; size overflow)";
         case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";
         default: return "unknown status";
     }

@@ -96,8 +96,10 @@ typedef enum {
  * q      device, E4M3 codes [rows, cols], written
  * scale  device, fp32 [rows], written
  * rows, cols >= 0; rows == 0 is a no-op; cols == 0 writes scale = 0.
+ * rows >= 2^31 -> ERR_UNSUPPORTED.
  * NaN/Inf in x are outside the contract.  Bit-exact with the definition.
- * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_ALIGN, ERR_OVERLAP, ERR_HIP.
+ * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_ALIGN, ERR_OVERLAP,
+ * ERR_UNSUPPORTED, ERR_HIP.
  */
 int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
                          uint8_t* q, float* scale, hipStream_t stream);
@@ -120,8 +122,10 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
  * scale_a  device, fp32 [m]                   scale_b device, fp32 [n]
  * D        device, [m, n] of out_dtype (fp8g_out_t), written
  * m, n, k >= 0.  m == 0 or n == 0: no-op.  k == 0: D = 0.
- * Limits: k % 16 != 0 -> ERR_UNSUPPORTED (16-byte rows).  E4M3 NaN codes in
- * A or B are outside the contract.
+ * Limits (ERR_UNSUPPORTED): k % 16 != 0 (16-byte rows); k >= 2^23, m >= 2^31,
+ * or n >= 2^22 (bf16 output) / 2^21 (fp32 output): the kernels address a
+ * 256-row panel of A, B or D with 32-bit offsets below 2^31.  E4M3 NaN codes
+ * in A or B are outside the contract.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP,
  * ERR_UNSUPPORTED, ERR_HIP.
  */
@@ -158,8 +162,9 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
  * scale    device, fp32, written: [rows] (FP8G_SCALE_PER_ROW) or [1]
  *          (FP8G_SCALE_PER_TENSOR; it holds an intermediate until the call's
  *          work on the stream has finished)
- * rows, cols >= 0.  Per row: rows == 0 is a no-op.  Per tensor: the scale is
- * always written (0 for an empty tensor).  Bit-exact with the definition.
+ * rows, cols >= 0.  Per row: rows == 0 is a no-op; rows >= 2^31 ->
+ * ERR_UNSUPPORTED.  Per tensor: the scale is always written (0 for an empty
+ * tensor).  Bit-exact with the definition.
  * Errors: ERR_NULL, ERR_SHAPE (negative), ERR_DTYPE (unknown in_dtype,
  * granularity or out_fmt), ERR_ALIGN, ERR_OVERLAP, ERR_UNSUPPORTED (size
  * overflow), ERR_HIP.
@@ -213,8 +218,11 @@ int mxfp8_quantize(const float* x, int64_t rows, int64_t cols,
  * scale_a  device, UE8M0 codes [m, k/32]      scale_b device, UE8M0 codes [n, k/32]
  * D        device, [m, n] of out_dtype, written
  * k % 32 != 0 -> ERR_SHAPE.  m == 0 or n == 0: no-op.  k == 0: D = 0.
+ * Limits as fp8_gemm_scaled: k >= 2^23, m >= 2^31, n >= 2^22 (bf16) / 2^21
+ * (fp32) -> ERR_UNSUPPORTED.
  * Scale code 255 (NaN) and E4M3 NaN codes are outside the contract.
- * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP, ERR_HIP.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP,
+ * ERR_UNSUPPORTED, ERR_HIP.
  */
 int mxfp8_gemm(int64_t m, int64_t n, int64_t k,
                const uint8_t* A, const uint8_t* B,

@@ -105,6 +105,30 @@ def test_huge_sizes_rejected(lib):
     assert gemm(lib, "fp8_gemm_scaled", 1 << 40, 1 << 40, 1 << 20) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex"])
+def test_gemm_32bit_panel_limits(lib, fn):
+    """k < 2^23, m < 2^31, and a 256-row panel of D below 2^31 bytes: n < 2^22
+    for bf16 output, n < 2^21 for fp32 output.  Just inside each limit the call
+    passes the host checks (and fails only at the launch, without a GPU)."""
+    far = 1 << 44                                   # operands far apart: no overlap at these sizes
+    kw = dict(B=P_(far), sa=P_(2 * far), sb=P_(3 * far), D=P_(4 * far))
+    assert gemm(lib, fn, 4, 4, 1 << 23, **kw) == UNSUPPORTED
+    assert gemm(lib, fn, 4, 4, (1 << 23) - 128, **kw) in (OK, HIP)
+    assert gemm(lib, fn, 1 << 31, 4, 128, **kw) == UNSUPPORTED
+    assert gemm(lib, fn, 4, (1 << 22) + 1, 128, out=0, **kw) == UNSUPPORTED
+    assert gemm(lib, fn, 4, 1 << 22, 128, out=0, **kw) in (OK, HIP)
+    assert gemm(lib, fn, 4, (1 << 21) + 1, 128, out=1, **kw) == UNSUPPORTED
+    assert gemm(lib, fn, 4, 1 << 21, 128, out=1, **kw) in (OK, HIP)
+
+
+def test_quantize_rows_limit(lib):
+    far = 1 << 44
+    assert lib.fp8_quantize_rowwise(P_(0), 1 << 31, 1, P_(far), P_(2 * far), ctypes.c_void_p(S)) == UNSUPPORTED
+    assert lib.fp8_quantize_ex(P_(0), 0, 1 << 31, 1, 0, 0, P_(far), P_(2 * far), ctypes.c_void_p(S)) == UNSUPPORTED
+    # per tensor has no per-row grid: the same extent passes the host checks
+    assert lib.fp8_quantize_ex(P_(0), 0, 1 << 31, 1, 1, 0, P_(far), P_(2 * far), ctypes.c_void_p(S)) in (OK, HIP)
+
+
 def quant(lib, x=P_(0), rows=8, cols=64, q=P_(1 << 30), s=P_(2 << 30)):
     return lib.fp8_quantize_rowwise(x, rows, cols, q, s, ctypes.c_void_p(S))
 
