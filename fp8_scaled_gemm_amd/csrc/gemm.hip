@@ -19,10 +19,14 @@
 //
 // Tiling: a 256-thread workgroup (4 waves, 2x2) owns a 256x256 output tile;
 // each wave owns 128x128 = 4x4 blocks of the 32x32 matrix-core tile (256 fp32
-// accumulators per lane).  K is walked in 64-byte steps, one
-// V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block per step; mode (a) passes the
-// neutral scale code 127 (2^0) and applies sa, sb in the epilogue, mode (b)
-// passes the operands' block scales.
+// accumulators per lane).  Problems with at most half as many 256x256 tiles as
+// CUs (2048 x 1024: 32 tiles for 256 CUs) use 128x128 tiles instead (waves of
+// 64x64 = 2x2 blocks): four times the workgroups, each moving twice the
+// operand bytes per flop, which the idle CUs more than pay for.
+//
+// K is walked in 64-byte steps, one V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block
+// per step; mode (a) passes the neutral scale code 127 (2^0) and applies sa,
+// sb in the epilogue, mode (b) passes the operands' block scales.
 //
 // Persistent workgroups: one per CU, each walking a list of tiles.  Its
 // stages (128 bytes of K, two steps) form one stream across its tiles, so the
@@ -82,41 +86,54 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256;        // tile rows (m)
-constexpr int BN = 256;        // tile cols (n)
 constexpr int BK = 128;        // bytes of K per stage (two matrix-core steps)
 constexpr int KSTEP = 64;      // bytes of K per matrix-core step
 constexpr int NTHREADS = 256;
-constexpr int WT = 128;        // wave tile edge
-constexpr int NB = WT / 32;    // 32x32 blocks per wave-tile edge
 constexpr int NUM_XCD = 8;
 constexpr int GROUP_M = 8;
 
-constexpr int OP_BYTES = BM * BK;      // 32 KB: one operand of one stage (an "item")
-constexpr int SCALE_BYTES = BM * 4;    // mode (b): the stage's 4 block scales of every row, one dword
-constexpr int DMA_PER_ITEM = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 8
+// Tile geometry: a TILE x TILE output tile per workgroup (TILE = 256, or 128
+// for problems with few tiles), 4 waves in 2x2, each wave WT x WT = NB x NB
+// blocks of 32x32.
+template <int TILE>
+struct Geo {
+    static constexpr int WT = TILE / 2;                        // wave tile edge
+    static constexpr int NB = WT / 32;                         // blocks per wave-tile edge: 4 or 2
+    static constexpr int OP_BYTES = TILE * BK;                 // one operand of one stage (an "item"): 32 or 16 KB
+    static constexpr int SCALE_BYTES = TILE * 4;               // mode (b): the stage's 4 block scales of every row
+    static constexpr int DMA_PER_ITEM = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 8 or 4
+};
 
-// Ring geometry per kernel variant: mode (b) with whole scale dwords keeps each
-// item's scales beside it (4 slots of 33 KB); otherwise 5 slots of 32 KB.
-template <bool MX, bool KTAIL>
+// Ring geometry per kernel variant.  256-row items: 5 slots of 32 KB fill the
+// LDS, so mode (b) with whole scale dwords (each item's scales beside it)
+// fits only 4 slots of 33 KB.  128-row items: 5 slots of 16 (16.5) KB.
+template <bool MX, bool KTAIL, int TILE>
 struct Ring {
+    using G = Geo<TILE>;
     static constexpr bool SCALES = MX && !KTAIL;
-    static constexpr int NSLOT = SCALES ? 4 : 5;
-    static constexpr int SLOT = OP_BYTES + (SCALES ? SCALE_BYTES : 0);
+    static constexpr int NSLOT = (SCALES && TILE == 256) ? 4 : 5;
+    static constexpr int SLOT = G::OP_BYTES + (SCALES ? G::SCALE_BYTES : 0);
     static constexpr int LDS = NSLOT * SLOT;
-    static constexpr int LOADS = DMA_PER_ITEM + (SCALES ? 1 : 0);   // load instructions per item and wave
+    static constexpr int LOADS = G::DMA_PER_ITEM + (SCALES ? 1 : 0);   // load instructions per item and wave
     // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
     // slots are free (its step 1), so both its items are issued in that step
     // (none in step 0) to give them the longest lead.  5 slots: one item per
     // step, four items ahead.
     static constexpr bool PAIRED = NSLOT == 4;
-    // bf16 epilogue staging (16 KB): 5 slots borrow the slot that is free
-    // during the epilogue; 4 (paired) slots have none free, so a region after
-    // the ring is used
+    // bf16 epilogue staging (16 KB, and the tile's sa, sb at +16 KB): with 5
+    // slots of 32 KB the slot that is free during the epilogue is borrowed;
+    // otherwise (paired, or 16 KB slots) a region after the ring is used
+    static constexpr bool OWN_STAGE = PAIRED || TILE != 256;
     static constexpr int STAGE_AREA = LDS;
-    static constexpr int LDS_TOTAL = LDS + (PAIRED ? 16 * 1024 : 0);
+    static constexpr int LDS_TOTAL = LDS + (OWN_STAGE ? 18 * 1024 : 0);
 };
-static_assert(Ring<false, false>::LDS_TOTAL <= 160 * 1024 && Ring<true, false>::LDS_TOTAL <= 160 * 1024, "LDS");
+static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
+                  Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024, "LDS");
+
+// The share of n items that slot k of s slots takes: one per slot while they
+// last when s >= n, else an even split.
+__host__ __device__ constexpr int share_lo(int k, int n, int s) { return s >= n ? (k < n ? k : n) : k * n / s; }
+__host__ __device__ constexpr int share_hi(int k, int n, int s) { return s >= n ? (k < n ? k + 1 : n) : (k + 1) * n / s; }
 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
 
@@ -169,12 +186,15 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
 
 // FA, FB: format code of A and of B (0 = E4M3, 1 = E5M2, as the instruction's
 // format fields)
-template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB>
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const float* __restrict__ sa, const float* __restrict__ sb, const uint8_t* __restrict__ ea,
     const uint8_t* __restrict__ eb, void* __restrict__ Dv) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    using GEO = Geo<TILE>;
+    constexpr int BM = TILE, BN = TILE, WT = GEO::WT, NB = GEO::NB;
+    constexpr int OP_BYTES = GEO::OP_BYTES, DMA_PER_ITEM = GEO::DMA_PER_ITEM;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -205,14 +225,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // walks the items; descriptors change once per tile.  Past the end of the
     // stream the last stage is loaded again (never read), so every K step
     // issues the same number of loads.
-    using R = Ring<MX, KTAIL>;
+    using R = Ring<MX, KTAIL, TILE>;
     constexpr int NSLOT = R::NSLOT, SLOT = R::SLOT, LI = R::LOADS;
     // lane L of wave w, instruction p fills row 32p + 8w + L/8, slot L%8, which
     // holds logical chunk (L%8) ^ ((row >> 1) & 7) = (L%8) ^ ((4w + L/16) & 7)
     const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
     const uint32_t dma_voff = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)K + dma_chunk * 16u;
-    // mode (b) scales: dword loads, lane L of wave w fills row 64w + L
-    const uint32_t sdma_voff = (uint32_t)(64 * wave + lane) * (uint32_t)nblk;
+    // mode (b) scales: dword loads, lane L of wave w fills row 64w + L; with
+    // 128-row items waves 2, 3 repeat the loads of waves 0, 1 (same bytes to the
+    // same place), so that every wave issues the same number of loads per item
+    constexpr int SW = TILE / 64;   // waves with distinct scale rows
+    const uint32_t sdma_voff = (uint32_t)(64 * (wave % SW) + lane) * (uint32_t)nblk;
     constexpr uint32_t OOB_OFF = 0x80000000u;   // past any panel (panels are < 2^31 bytes)
     int ij = 0, is = 0, iop = 0, ii = 0, islot = 0;   // cursor: tile, stage in tile, operand, item, its slot
     __amdgpu_buffer_rsrc_t rsA, rsB, rsEA, rsEB;
@@ -241,7 +264,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             const uint32_t so = uniform(k0 + (uint32_t)(32 * q) * (uint32_t)K);
             dma16(uniform(sbuf + (uint32_t)((4 * q + wave) * 1024)), voff, iop ? rsB : rsA, so);
         } else if constexpr (R::SCALES) {
-            dma4(uniform(sbuf + (uint32_t)(OP_BYTES + wave * 256)), sdma_voff, iop ? rsEB : rsEA,
+            dma4(uniform(sbuf + (uint32_t)(OP_BYTES + (wave % SW) * 256)), sdma_voff, iop ? rsEB : rsEA,
                  uniform((uint32_t)(4 * s_ld)));
         }
     };
@@ -455,7 +478,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int rr = lane_e >> 3;                          // read-back: row within 8
         const uint32_t rd_off = (uint32_t)(rr * 128) + ((rc ^ (uint32_t)((rr >> 1) & 3)) << 4);
 #pragma unroll
-        for (int ih = 0; ih < 2; ++ih) {          // column half of the wave tile: blocks i = 2ih, 2ih+1
+        for (int ih = 0; ih < NB / 2; ++ih) {     // 64-column part of the wave tile: blocks i = 2ih, 2ih+1
             float snv[2][4][4];
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
@@ -566,6 +589,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   matrix-core steps behind a burst of loads from all four waves.
     //   LAST (the tile's last step): no reads of the next step's fragments (they
     //   are read after the epilogue, which then has their registers to itself).
+    // matrix-core steps after row block 0 (12, or 2 for 128-row tiles); the
+    // step's loads and the next step's 2 NB fragment reads are spread over them
+    constexpr int SLOTS = (NB - 1) * NB;
+    constexpr int NREAD = 2 * NB;
+    constexpr int SCALE_SLOT = SLOTS > NREAD ? NREAD + 1 : SLOTS - 1;
     auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
                      v8i* nbf) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
@@ -582,7 +610,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             // staged epilogue (before this step's item loads, so that waiting for
             // all but those leaves the scales landed)
             if constexpr (!MX && LAST) {
-                if (staged) tile_scales_to_lds(g / nk, (uint32_t)(slot_add(rslot, 1) * SLOT));
+                if (staged)
+                    tile_scales_to_lds(g / nk, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -591,24 +620,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const uint32_t sa_off = (uint32_t)(na_slot * SLOT), sb_off = (uint32_t)(slot_add(na_slot, 1) * SLOT);
         uint32_t nxa[NB], nxb[NB];
 #pragma unroll
-        for (int k = 0; k < 12; ++k) {
-            const int i = 1 + k / 4, jb = k % 4;
+        for (int k = 0; k < SLOTS; ++k) {
+            const int i = 1 + k / NB, jb = k % NB;
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
             if constexpr (!R::PAIRED) {
-                if (k < LI) dma_item(k);
-            } else if (h == 1) {
-                // the stage's two items: the first over slots 0-5, the second over 6-11
-                const int kk = k % 6;
 #pragma unroll
-                for (int q = kk * LI / 6; q < (kk + 1) * LI / 6; ++q) dma_item(q);
-                if (k == 5) advance();
+                for (int q = share_lo(k, LI, SLOTS); q < share_hi(k, LI, SLOTS); ++q) dma_item(q);
+            } else if (h == 1) {
+                // the stage's two items: the first over the first half of the slots, the second over the rest
+                constexpr int HALF = SLOTS / 2;
+                const int kk = k % HALF;
+#pragma unroll
+                for (int q = kk * LI / HALF; q < (kk + 1) * LI / HALF; ++q) dma_item(q);
+                if (k == HALF - 1) advance();
             }
-            // reads in order of first use: row block 0 of B, the four of A, then B 1..3
+            // reads in order of first use: row block 0 of B, the NB of A, then the rest of B
             if constexpr (!LAST) {
-                if (k == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
-                if (k >= 1 && k <= 4) na[k - 1] = frag(sa_off, frag_a, hn, k - 1);
-                if (k >= 5 && k <= 7) nbf[k - 4] = frag(sb_off, frag_b, hn, k - 4);
-                if (k == 9) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+#pragma unroll
+                for (int e = share_lo(k, NREAD, SLOTS); e < share_hi(k, NREAD, SLOTS); ++e) {
+                    if (e == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
+                    else if (e <= NB) na[e - 1] = frag(sa_off, frag_a, hn, e - 1);
+                    else nbf[e - NB] = frag(sb_off, frag_b, hn, e - NB);
+                }
+                if (k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -647,7 +681,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             // loads into it (every wave finished reading it before the last barrier)
             if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
-            epilogue_staged(j, acc, R::PAIRED ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
+            epilogue_staged(j, acc, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
             __syncthreads();   // staging reads done before that slot is loaded again
         } else {
             epilogue(j, acc);
@@ -665,12 +699,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     wait_vmcnt<0>();   // the past-the-end loads must land before the workgroup exits
 }
 
-template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB>
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE>
 static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
-                             hipStream_t stream) {
-    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB>;
-    constexpr int LDS_BYTES = Ring<MX, KTAIL>::LDS_TOTAL;
+                             int cus, hipStream_t stream) {
+    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB, TILE>;
+    constexpr int LDS_BYTES = Ring<MX, KTAIL, TILE>::LDS_TOTAL;
     // up to 160 KB of dynamic LDS is above the default launch limit; raise it once.
     static std::once_flag once;
     static hipError_t attr_status = hipSuccess;
@@ -679,30 +713,41 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     });
     if (attr_status != hipSuccess) return attr_status;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
     const int64_t grid = tiles < cus ? tiles : cus;   // persistent: at most one workgroup per CU
     kern<<<dim3((unsigned)grid), dim3(NTHREADS), LDS_BYTES, stream>>>((int)m, (int)n, (int)k, A, B, sa, sb, ea,
                                                                       eb, D);
     return hipGetLastError();
 }
 
-template <bool MX, int FA, int FB>
-hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
-                      const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
-                      hipStream_t stream) {
+template <bool MX, int FA, int FB, int TILE>
+static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
+                               const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, int cus,
+                               hipStream_t stream) {
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
     if (out_f32)
-        return tail ? launch_one<MX, true, true, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
-                    : launch_one<MX, true, false, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
-    return tail ? launch_one<MX, false, true, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream)
-                : launch_one<MX, false, false, FA, FB>(m, n, k, A, B, sa, sb, ea, eb, D, stream);
+        return tail ? launch_one<MX, true, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream)
+                    : launch_one<MX, true, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream);
+    return tail ? launch_one<MX, false, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream)
+                : launch_one<MX, false, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream);
+}
+
+template <bool MX, int FA, int FB>
+hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
+                      const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
+                      hipStream_t stream) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // 128-row tiles when 256-row tiles would leave at least half of the CUs
+    // idle: four times the tiles, each at a lower matrix-core rate
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    if (2 * tiles256 <= cus) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, cus, stream);
+    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, cus, stream);
 }
 
 // Each operand-format pair's kernels may be compiled in an object of their
@@ -753,7 +798,7 @@ static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A,
 // 32-bit buffer offsets: a 256-row panel of K bytes stays below 2^31, so the
 // out-of-range offset 2^31 plus any scalar offset still fits in 32 bits.
 static bool fits(int64_t m, int64_t n, int64_t k) {
-    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
     return m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 23) && tiles < (1LL << 31);
 }
 

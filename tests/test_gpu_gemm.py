@@ -50,9 +50,12 @@ def uscale(seed, n, stream=3):
 
 
 # (M, N, K): tile-aligned, ragged in m/n, a K tail that is not a multiple of the
-# 128-byte stage, single elements, several tiles in both directions.
+# 128-byte stage, single elements, several tiles in both directions.  Problems
+# with at most half as many 256x256 tiles as CUs run on 128x128 tiles: the
+# last two shapes have more (2561 x 3000: 11 x 12 tiles of 256) and take the
+# 256x256 kernels, with ragged m, n and a K tail.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
-            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272)]
+            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (2561, 3000, 272), (2600, 2900, 1024)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -185,7 +188,7 @@ def mx_scales(seed, R, nb, stream):
 
 
 SHAPES_B = [(32, 32, 32), (64, 96, 96), (256, 256, 256), (257, 300, 4128), (512, 512, 1024), (5, 700, 160),
-            (300, 7, 64)]
+            (300, 7, 64), (2561, 3000, 1056), (2600, 2900, 1024)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])

@@ -63,8 +63,9 @@ def check_scaled(fp8g, A, fa, B, fb, sa, sb, out, what):
                              out, what, gemm.alignment_term(A, B, sa, sb, fmt_a=na, fmt_b=nb))
 
 
+# the last shape has more than half as many 256x256 tiles as CUs: 256x256 kernels
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (1, 513, 2048),
-            (1000, 1001, 272)]
+            (1000, 1001, 272), (2561, 3000, 272)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -140,7 +141,7 @@ def test_ex_dtype_checks(gpu_lib):
         gpu_lib.fp8_gemm_scaled_ex(4, 4, 64, A.view(torch.uint8), 2, B, E5M2, s, s)
 
 
-SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160)]
+SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160), (2600, 2900, 1024)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
