@@ -127,6 +127,11 @@ def _as_codes(t, name, fmt=FMT_E4M3):
 def _need(t, name, dtype=None, shape=None):
     if not t.is_cuda:
         raise ValueError("%s must be a device tensor" % name)
+    cur = _torch().cuda.current_device()
+    if t.device.index != cur:
+        # the kernels run on the current device and take raw pointers
+        raise ValueError("%s is on %s but the current device is cuda:%d (call under torch.cuda.device(%s))"
+                         % (name, t.device, cur, t.device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:

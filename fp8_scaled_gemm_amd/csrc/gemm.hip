@@ -73,7 +73,7 @@
 // with a partial EXEC mask yet still writes every lane.  Here they feed only
 // the accumulators and the epilogue, under uniform control flow.
 
-#include <mutex>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -702,17 +702,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE>
 static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
-                             int cus, hipStream_t stream) {
+                             int dev, int cus, hipStream_t stream) {
     auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB, TILE>;
     constexpr int LDS_BYTES = Ring<MX, KTAIL, TILE>::LDS_TOTAL;
-    // up to 160 KB of dynamic LDS is above the default launch limit; raise it once.
-    static std::once_flag once;
-    static hipError_t attr_status = hipSuccess;
-    std::call_once(once, [&] {
-        attr_status = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    });
-    if (attr_status != hipSuccess) return attr_status;
+    // up to 160 KB of dynamic LDS is above the default launch limit; raise it
+    // once per device (the attribute is set for the current device).  Setting
+    // it twice from racing threads is harmless.
+    static std::atomic<uint64_t> configured{0};
+    const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+    if (!bit || !(configured.load(std::memory_order_acquire) & bit)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        configured.fetch_or(bit, std::memory_order_release);
+    }
     const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
     const int64_t grid = tiles < cus ? tiles : cus;   // persistent: at most one workgroup per CU
     kern<<<dim3((unsigned)grid), dim3(NTHREADS), LDS_BYTES, stream>>>((int)m, (int)n, (int)k, A, B, sa, sb, ea,
@@ -722,16 +725,16 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
 
 template <bool MX, int FA, int FB, int TILE>
 static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
-                               const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, int cus,
-                               hipStream_t stream) {
+                               const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, int dev,
+                               int cus, hipStream_t stream) {
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
     if (out_f32)
-        return tail ? launch_one<MX, true, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream)
-                    : launch_one<MX, true, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream);
-    return tail ? launch_one<MX, false, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream)
-                : launch_one<MX, false, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, cus, stream);
+        return tail ? launch_one<MX, true, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream)
+                    : launch_one<MX, true, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream);
+    return tail ? launch_one<MX, false, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream)
+                : launch_one<MX, false, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream);
 }
 
 template <bool MX, int FA, int FB>
@@ -746,8 +749,8 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     // 128-row tiles when 256-row tiles would leave at least half of the CUs
     // idle: four times the tiles, each at a lower matrix-core rate
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-    if (2 * tiles256 <= cus) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, cus, stream);
-    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, cus, stream);
+    if (2 * tiles256 <= cus) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
+    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
 }
 
 // Each operand-format pair's kernels may be compiled in an object of their
