@@ -128,8 +128,9 @@ def cpu_baseline_mx(w, m_s=2048, n_s=8192):
 
 TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic.txt",
                  "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt",
-                 "concat_mla": "profiles/concat_mla_k_fp8_16384x128_hbm_traffic.txt"}
-KERNEL_SOURCES = {"ffn_up": "gemm.hip", "mx": "gemm.hip", "concat_mla": "concat.hip"}
+                 "concat_mla": "profiles/concat_mla_k_fp8_16384x128_hbm_traffic.txt",
+                 "quantize": "profiles/quantize_rows_f32_e4m3_8192x8192_hbm_traffic.txt"}
+KERNEL_SOURCES = {"ffn_up": "gemm.hip", "mx": "gemm.hip", "concat_mla": "concat.hip", "quantize": "quantize.hip"}
 
 
 def source_digest(name="gemm.hip"):
@@ -186,15 +187,17 @@ def concat_bench(args, torch, fp8g):
     for _ in range(args.warmup):
         fp8g.concat_mla_k(nope, rope, k)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # one event pair around the back-to-back launches on the stream (a pair per
+    # 100 us launch would add its own few us)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
+    e0.record(stream)
+    for _ in range(args.steps):
         fp8g.concat_mla_k(nope, rope, k)
-        e1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    us = e0.elapsed_time(e1) / args.steps * 1e3
     nbytes = T * H * 128 + T * 64 + T * H * 192
     ms = elapsed / args.steps * 1e3
     line = {"metric": "concat_mla_k GB/s (FP8, %d tokens x %d heads, rope shared)" % (T, H),
@@ -254,15 +257,17 @@ def quantize_bench(args, torch, fp8g):
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        # one event pair around the back-to-back launches on the stream: a pair
+        # per launch of a 50 us kernel adds several us of its own
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for e0, e1 in evs:
-            e0.record(stream)
+        e0.record(stream)
+        for _ in range(args.steps):
             call()
-            e1.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        us = e0.elapsed_time(e1) / args.steps * 1e3
         nbytes = R * C * ((2 if bf else 4) + 1) + (4 if pt else 4 * R)
         res[name] = {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes,
                      "ms_per_call": elapsed / args.steps * 1e3}
@@ -273,7 +278,8 @@ def quantize_bench(args, torch, fp8g):
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "quantize_ffn_up_activations_8192x8192", "rows": R, "cols": C},
             "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(head["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                         "frac": round(head["gbs"] / PEAK_HBM_GBS, 4),
+                         "traffic": read_traffic(os.path.join(ROOT, TRAFFIC_FILES["quantize"]), "quantize.hip"),
                          "kernel": "quantize_rows_wg", "bytes_per_launch": head["bytes"]},
             "modes": {k: {"us": v["us"], "gbs": v["gbs"], "frac": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                       for k, v in res.items()}}
