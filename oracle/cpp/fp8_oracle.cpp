@@ -1,0 +1,219 @@
+// Plain C++ oracle -- test infrastructure (never linked into the library).
+//
+// The same definitions as the numpy oracle (oracle/*.py), written again
+// independently in plain scalar C++ with double-precision accumulation, so
+// that the two can be checked against each other and the cast can be checked
+// exhaustively over all 2^32 fp32 bit patterns.
+//
+//   * FP8 decode from the bit fields: OCP E4M3FN (bias 7, NaN only at
+//     S.1111.111, largest 448 -- the constant of `_calibrate_scales` on the
+//     page "FP8 推理基础设施（五）：从 DeepGEMM 到 vLLM") and OCP E5M2 (bias 15,
+//     IEEE-style Inf/NaN, largest 57344 -- the second FP8 type of the page on
+//     FlashInfer's concat_mla_k with FP8 inputs).
+//   * The saturating round-to-nearest-even cast, twice: as the definition
+//     (the nearest of the format's decoded magnitudes, ties to the even code)
+//     and as integer bit manipulation of the fp32 input.
+//   * The row-wise quantizer: s = fp32(amax / MAX), q = cast(fp32(x / s)).
+//   * Mode (a): D = sa[m] sb[n] sum_k dec(A[m,k]) dec(B[n,k]) in double, and
+//     mode (b): D = sum_j 2^(ea+eb-254) sum_{t<32} dec dec (page "[sglang]
+//     FlashInfer v0.6.7 MXFP8 Gemm 통합", sections 1-2), plain loops.
+//
+// Build: g++ -O2 -shared -fPIC (no vector intrinsics).  C entry points only.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+namespace {
+
+// format description: exponent bits, mantissa bits, bias, IEEE-style specials
+struct Fmt {
+    int ebits, mbits, bias;
+    bool ieee;      // true: all-ones exponent is Inf/NaN (E5M2); false: only S.1111.111 is NaN (E4M3FN)
+    int max_code;   // largest finite magnitude code (0x7E / 0x7B)
+};
+constexpr Fmt E4M3{4, 3, 7, false, 0x7E};
+constexpr Fmt E5M2{5, 2, 15, true, 0x7B};
+
+const Fmt& fmt_of(int f) { return f == 1 ? E5M2 : E4M3; }
+
+double decode(const Fmt& F, uint8_t c) {
+    const int s = c >> 7;
+    const int e = (c >> F.mbits) & ((1 << F.ebits) - 1);
+    const int m = c & ((1 << F.mbits) - 1);
+    const int emax = (1 << F.ebits) - 1;
+    double mag;
+    if (F.ieee && e == emax) {
+        mag = m == 0 ? INFINITY : NAN;
+    } else if (!F.ieee && e == emax && m == (1 << F.mbits) - 1) {
+        mag = NAN;
+    } else if (e == 0) {
+        mag = std::ldexp((double)m, 1 - F.bias - F.mbits);
+    } else {
+        mag = std::ldexp((double)((1 << F.mbits) + m), e - F.bias - F.mbits);
+    }
+    return s ? -mag : mag;
+}
+
+float bits_to_float(uint32_t u) {
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+uint32_t float_to_bits(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return u;
+}
+
+// The non-negative finite magnitudes of a format, codes 0 .. max_code (ascending).
+struct Mags {
+    double v[128];
+    explicit Mags(const Fmt& F) {
+        for (int c = 0; c <= F.max_code; ++c) v[c] = decode(F, (uint8_t)c);
+    }
+};
+const Mags& mags_of(const Fmt& F) {
+    static const Mags e4(E4M3), e5(E5M2);   // initialised once (thread-safe)
+    return F.ebits == 5 ? e5 : e4;
+}
+
+// The definition: nearest of the non-negative finite magnitudes, ties to the
+// even code, saturating, sign copied; NaN gives 0x7F with the sign.
+uint8_t encode_nearest(const Fmt& F, float x) {
+    const uint8_t sign = (uint8_t)(float_to_bits(x) >> 31) << 7;
+    if (std::isnan(x)) return (uint8_t)(0x7F | sign);
+    const double* mag = mags_of(F).v;
+    const double a = std::fabs((double)x);
+    if (a >= mag[F.max_code]) return (uint8_t)(F.max_code | sign);
+    int lo = 0, hi = F.max_code;   // mag[lo] <= a < mag[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (mag[mid] <= a) lo = mid; else hi = mid;
+    }
+    const double mid = (mag[lo] + mag[hi]) * 0.5;   // exact in double
+    int c;
+    if (a > mid) c = hi;
+    else if (a < mid) c = lo;
+    else c = (lo % 2 == 0) ? lo : hi;
+    return (uint8_t)(c | sign);
+}
+
+// The same cast by integer arithmetic on the fp32 fields: align the 24-bit
+// significand to the code's last mantissa place and round half to even.
+uint8_t encode_bits(const Fmt& F, float x) {
+    const uint32_t u = float_to_bits(x);
+    const uint8_t sign = (uint8_t)(u >> 31) << 7;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint8_t)(0x7F | sign);                       // NaN
+    const uint32_t top = float_to_bits((float)mags_of(F).v[F.max_code]);
+    if (a >= top) return (uint8_t)(F.max_code | sign);                         // saturate (Inf too)
+    if (a < 0x00800000u) return sign;                                          // zero, fp32 subnormal: below half the smallest code
+    const int e = (int)(a >> 23) - 127;                                        // x = sig * 2^(e-23)
+    const uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;
+    const int emin = 1 - F.bias;                                               // smallest normal exponent
+    // target unit: 2^(e - mbits) for normals, 2^(emin - mbits) below them
+    const int unit = (e >= emin ? e : emin) - F.mbits;
+    const int shift = 23 - (e - unit);                                         // sig >> shift = x / 2^unit
+    uint32_t q;
+    if (shift >= 32) {
+        q = 0;                                                                 // far below half a unit
+    } else {
+        q = sig >> shift;
+        const uint32_t rem = sig & ((1u << shift) - 1u);
+        const uint32_t half = 1u << (shift - 1);
+        if (rem > half || (rem == half && (q & 1u))) ++q;
+    }
+    // q counts units of 2^unit: for normals 2^mbits <= q <= 2^(mbits+1)
+    // (the top rolls into the next binade), below them q <= 2^mbits
+    uint32_t code;
+    if (e >= emin) {
+        int E = e + F.bias;
+        if (q == (2u << F.mbits)) { q >>= 1; ++E; }
+        code = ((uint32_t)E << F.mbits) | (q - (1u << F.mbits));
+    } else {
+        code = q;   // subnormal codes; q == 2^mbits is the smallest normal code
+    }
+    if (code > (uint32_t)F.max_code) code = (uint32_t)F.max_code;
+    return (uint8_t)(code | sign);
+}
+
+}  // namespace
+
+extern "C" {
+
+double fp8o_decode(int fmt, uint8_t c) { return decode(fmt_of(fmt), c); }
+uint8_t fp8o_encode_nearest(int fmt, float x) { return encode_nearest(fmt_of(fmt), x); }
+uint8_t fp8o_encode_bits(int fmt, float x) { return encode_bits(fmt_of(fmt), x); }
+
+// Every fp32 pattern in [lo, hi): both casts; returns the number of patterns
+// where they differ and the first one in *first (unchanged if none).
+int64_t fp8o_cast_sweep(int fmt, uint64_t lo, uint64_t hi, uint32_t* first) {
+    const Fmt& F = fmt_of(fmt);
+    int64_t bad = 0;
+    for (uint64_t p = lo; p < hi; ++p) {
+        const float x = bits_to_float((uint32_t)p);
+        if (encode_nearest(F, x) != encode_bits(F, x)) {
+            if (bad == 0 && first) *first = (uint32_t)p;
+            ++bad;
+        }
+    }
+    return bad;
+}
+
+// Batch cast (definition) of n floats.
+void fp8o_encode_array(int fmt, const float* x, int64_t n, uint8_t* q) {
+    const Fmt& F = fmt_of(fmt);
+    for (int64_t i = 0; i < n; ++i) q[i] = encode_nearest(F, x[i]);
+}
+
+// Row-wise quantizer: s[r] = fp32(max_c |x| / MAX); q = cast(fp32(x / s)); s == 0 gives signed zeros.
+void fp8o_quantize_rowwise(int fmt, const float* x, int64_t rows, int64_t cols, uint8_t* q, float* s) {
+    const Fmt& F = fmt_of(fmt);
+    const float maxv = (float)mags_of(F).v[F.max_code];
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) amax = std::fmax(amax, std::fabs(x[r * cols + c]));
+        const float sr = amax / maxv;
+        s[r] = sr;
+        for (int64_t c = 0; c < cols; ++c) {
+            const float v = x[r * cols + c];
+            const float y = sr == 0.0f ? std::copysign(0.0f, v) : v / sr;
+            q[r * cols + c] = encode_nearest(F, y);
+        }
+    }
+}
+
+// Mode (a) in double: D[m,n] = sa[m] sb[n] sum_k dec(A[m,k]) dec(B[n,k]).
+void fp8o_gemm_scaled(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
+                      const float* sa, const float* sb, double* D) {
+    const Fmt& FA = fmt_of(fmt_a);
+    const Fmt& FB = fmt_of(fmt_b);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += decode(FA, A[m * K + k]) * decode(FB, B[n * K + k]);
+            D[m * N + n] = acc * (double)sa[m] * (double)sb[n];
+        }
+}
+
+// Mode (b) in double: D[m,n] = sum_j 2^(ea[m,j]-127) 2^(eb[n,j]-127) sum_{t<32} dec(A) dec(B).
+void fp8o_gemm_mx(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
+                  const uint8_t* ea, const uint8_t* eb, double* D) {
+    const Fmt& FA = fmt_of(fmt_a);
+    const Fmt& FB = fmt_of(fmt_b);
+    const int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < nb; ++j) {
+                double blk = 0.0;
+                for (int64_t t = 0; t < 32; ++t)
+                    blk += decode(FA, A[m * K + 32 * j + t]) * decode(FB, B[n * K + 32 * j + t]);
+                acc += std::ldexp(blk, (int)ea[m * nb + j] + (int)eb[n * nb + j] - 254);
+            }
+            D[m * N + n] = acc;
+        }
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+"""Pins for the plain C++ oracle (oracle/cpp/fp8_oracle.cpp), CPU only.
+
+  * The cast on every one of the 2^32 fp32 bit patterns, E4M3 and E5M2: the
+    definition (nearest decoded magnitude, ties to the even code, saturating)
+    against an independent integer bit-manipulation of the same rounding.
+  * The two oracles (C++ and numpy) against each other: the 256-entry decode
+    tables, the cast on random patterns and on every rounding boundary, the
+    row-wise quantizer (bit for bit) and both GEMM modes.
+"""
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import cpp_oracle, e4m3, e5m2, gemm, quant
+
+FMTS = {"e4m3": e4m3, "e5m2": e5m2}
+
+
+def test_decode_tables_agree():
+    for name, mod in FMTS.items():
+        t = cpp_oracle.decode_table(name)
+        ref = mod.DECODE_TABLE
+        assert np.array_equal(np.isnan(t), np.isnan(ref)), name
+        ok = ~np.isnan(ref)
+        assert np.array_equal(t[ok], ref[ok]), name
+        assert np.array_equal(np.signbit(t[ok]), np.signbit(ref[ok])), name
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_cast_every_fp32_pattern(fmt):
+    """All 2^32 patterns: the definitional cast equals the bit-level cast."""
+    chunk = 1 << 26
+    starts = range(0, 1 << 32, chunk)
+    with ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as pool:
+        res = list(pool.map(lambda lo: (lo, cpp_oracle.cast_sweep(lo, lo + chunk, fmt)), starts))
+    bad = [(lo, r) for lo, r in res if r[0]]
+    assert not bad, "first mismatching pattern 0x%08x (%d in that chunk)" % (bad[0][1][1], bad[0][1][0])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_cast_agrees_with_numpy_oracle(fmt):
+    mod = FMTS[fmt]
+    rng = np.random.default_rng(5)
+    x = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    x = x[~np.isnan(x)]
+    mags = mod.DECODE_TABLE[:mod.MAX_CODE + 1]
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf))])
+    x = np.concatenate([x, near, -near, np.float32([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45])])
+    assert np.array_equal(cpp_oracle.encode(x, fmt), mod.encode(x))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantize_rowwise_agrees(fmt):
+    w = synth.WORKLOADS["c4_ffn_up_8192x22016x8192"]
+    x = synth.draw(w, "a", slice(0, 48))[:, :1000].copy()
+    t = np.float32(2.0 ** -149)
+    x[0] = 0.0
+    x[1, :3] = [t, -t, 0.0]
+    x[2] *= np.float32(1e-36)
+    x[3] *= np.float32(1e30)
+    q1, s1 = cpp_oracle.quantize_rowwise(x, fmt)
+    q2, s2 = quant.quantize_rowwise(x, fmt)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(q1, q2)
+
+
+def _codes(seed, shape, fmt):
+    c = synth.u8_codes(seed, 1, shape, exclude_nan=False)
+    if fmt == "e5m2":
+        return np.where((c & 0x7C) == 0x7C, c & 0xF3, c).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 1, c).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2")])
+def test_gemms_agree(fa, fb):
+    M, N, K = 7, 9, 160
+    A, B = _codes(31, (M, K), fa), _codes(32, (N, K), fb)
+    sa = (0.5 + synth.uniform(synth.stream_key(33, 1), 0, M)).astype(np.float32)
+    sb = (0.5 + synth.uniform(synth.stream_key(33, 2), 0, N)).astype(np.float32)
+    D1 = cpp_oracle.gemm_scaled(A, B, sa, sb, fa, fb)
+    D2 = gemm.gemm_scaled(A, B, sa, sb, fa, fb)
+    W = gemm.gemm_scaled_weight(A, B, sa, sb, fa, fb)
+    if fa == fb == "e4m3":
+        assert np.array_equal(D1, D2)          # both exact sums, the same two roundings
+    else:
+        assert np.all(np.abs(D1 - D2) <= (2 * K + 4) * 2.0 ** -53 * W)
+    ea = (synth.u8_codes(34, 3, (M, K // 32)) % 41 + 107).astype(np.uint8)
+    eb = (synth.u8_codes(35, 4, (N, K // 32)) % 41 + 107).astype(np.uint8)
+    X1 = cpp_oracle.mxfp8_gemm(A, B, ea, eb, fa, fb)
+    X2 = gemm.mxfp8_gemm(A, B, ea, eb, fa, fb)
+    XW = gemm.mxfp8_gemm_weight(A, B, ea, eb, fa, fb)
+    assert np.all(np.abs(X1 - X2) <= (2 * K + 4) * 2.0 ** -53 * XW)
