@@ -46,7 +46,7 @@ int check_gemm_common(int64_t m, int64_t n, int64_t k, const void* A, const void
     if (a_bytes < 0 || b_bytes < 0 || d_bytes < 0) return FP8G_ERR_UNSUPPORTED;
     // the kernels address a 256-row panel of A, B (k bytes per row) or D (n
     // elements per row) with 32-bit offsets below 2^31
-    if (k >= GEMM_K_LIMIT || m >= ((int64_t)1 << 31) || n * 256 * esz > ((int64_t)1 << 31))
+    if (k >= GEMM_K_LIMIT || m >= ((int64_t)1 << 31) || n > (((int64_t)1 << 31) / (256 * esz)))
         return FP8G_ERR_UNSUPPORTED;
     if (!D) return FP8G_ERR_NULL;
     if (k > 0 && (!A || !B)) return FP8G_ERR_NULL;
@@ -170,9 +170,9 @@ const char* fp8g_status_string(int status) {
         case FP8G_ERR_NULL: return "a required pointer is NULL";
         case FP8G_ERR_SHAPE: return "invalid shape (negative extent, or k / cols not a multiple of 32 for MXFP8)";
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case FP8G_ERR_DTYPE: return "unknown output dtype, input dtype, granularity or element size";
+        case FP8G_ERR_DTYPE: return "unknown output dtype, operand format, input dtype, granularity or element size";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
-        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (GEMM: k % 16, k >= 2^23, a 256-row panel of D of 2^31 bytes or more; rows >= 2^31; size overflow)";
+        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (GEMM: k % 16, k >= 2^23, m >= 2^31, a 256-row panel of D over 2^31 bytes; quantizer rows >= 2^31; size overflow)";
         case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";
         default: return "unknown status";
     }

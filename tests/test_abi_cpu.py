@@ -119,6 +119,8 @@ def test_gemm_32bit_panel_limits(lib, fn):
     assert gemm(lib, fn, 4, 1 << 22, 128, out=0, **kw) in (OK, HIP)
     assert gemm(lib, fn, 4, (1 << 21) + 1, 128, out=1, **kw) == UNSUPPORTED
     assert gemm(lib, fn, 4, 1 << 21, 128, out=1, **kw) in (OK, HIP)
+    # n so large that n * 256 * element size would overflow 64 bits: still rejected
+    assert gemm(lib, fn, 1, 1 << 55, 32, **kw) == UNSUPPORTED
 
 
 def test_quantize_rows_limit(lib):
