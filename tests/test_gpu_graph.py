@@ -1,0 +1,88 @@
+"""The hot path under HIP graph capture: quantize both operands and run the
+GEMM inside one captured graph (torch.cuda.CUDAGraph on the capture stream),
+replay it several times with eager work and synchronizations in between, and
+check every replay against the eager results bit for bit.  The library queues
+kernels only (no memsets, no allocation), so the whole path is capturable."""
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager(gpu_lib):
+    import torch
+    w = synth.Workload("graph", 520, 700, 1024, "a", "rowfactor_outlier", "normal", "rowwise", 41)
+    XA = torch.from_numpy(synth.draw(w, "a")).cuda()
+    XB = torch.from_numpy(synth.draw(w, "b")).cuda()
+    M, N, K = w.M, w.N, w.K
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M, device="cuda")
+    sb = torch.empty(N, device="cuda")
+    st = torch.empty(1, device="cuda")
+    qt = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Dt = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qm = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    em = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+
+    def path():
+        gpu_lib.fp8_quantize_rowwise(XA, qa, sa)
+        gpu_lib.fp8_quantize_rowwise(XB, qb, sb)
+        gpu_lib.fp8_gemm_scaled(M, N, K, qa, qb, sa, sb, D=D)
+        gpu_lib.fp8_quantize_ex(XB, per_tensor=True, q=qt, scale=st)       # clear, amax, cast, finish
+        gpu_lib.fp8_gemm_scaled(M, N, K, qa, qt, sa, st.expand(N).contiguous(), D=Dt, out_dtype=torch.float32)
+        gpu_lib.mxfp8_quantize(XA, qm, em)
+
+    outs = [qa, qb, sa, sb, st, qt, D, Dt, qm, em]
+    say("graph: eager")
+    path()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm up on the side stream, as capture needs
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    say("graph: capture")
+    with torch.cuda.graph(g):
+        path()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.zero_() if t.dtype != torch.bfloat16 else t.fill_(7.0)
+        junk = torch.randn(1 << 20, device="cuda") * 3            # eager work between replays
+        torch.cuda.synchronize()
+        say("graph: replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(["qa", "qb", "sa", "sb", "st", "qt", "D", "Dt", "qm", "em"], outs, eager):
+            assert torch.equal(t.view(torch.uint8) if t.dtype == torch.uint8 else t, e), (rep, name)
+        del junk
+
+
+def test_gemm_deterministic_both_tile_sizes(gpu_lib):
+    """Repeated launches give identical bits, on 256x256 tiles (2561 x 3000,
+    above the small-problem threshold) and on 128x128 tiles, in both modes."""
+    import torch
+    for (M, N, K) in ((2561, 3000, 1024), (700, 900, 1024)):
+        A = torch.from_numpy(synth.u8_codes(51, 1, (M, K))).cuda()
+        B = torch.from_numpy(synth.u8_codes(51, 2, (N, K))).cuda()
+        sa = torch.rand(M, device="cuda") + 0.5
+        sb = torch.rand(N, device="cuda") + 0.5
+        ea = torch.from_numpy((synth.u8_codes(51, 3, (M, K // 32)) % 41 + 107).astype(np.uint8)).cuda()
+        eb = torch.from_numpy((synth.u8_codes(51, 4, (N, K // 32)) % 41 + 107).astype(np.uint8)).cuda()
+        say("deterministic", M, N, K)
+        D1 = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb)
+        D2 = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb)
+        X1 = gpu_lib.mxfp8_gemm(M, N, K, A, B, ea, eb)
+        X2 = gpu_lib.mxfp8_gemm(M, N, K, A, B, ea, eb)
+        assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
+        assert torch.equal(X1.view(torch.int16), X2.view(torch.int16))
