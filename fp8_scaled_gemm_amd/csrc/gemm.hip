@@ -590,10 +590,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   LAST (the tile's last step): no reads of the next step's fragments (they
     //   are read after the epilogue, which then has their registers to itself).
     // matrix-core steps after row block 0 (12, or 2 for 128-row tiles); the
-    // step's loads and the next step's 2 NB fragment reads are spread over them
+    // step's loads and the next step's 2 NB fragment reads are spread over them.
+    // Mode (b) scales from LDS are read first, in slot 0: LDS reads complete in
+    // order, so scales read after the fragments would hold the next step's
+    // first matrix-core instruction until every fragment read had landed.
+    // Scales loaded byte-wise from global memory (K tail) are read after the
+    // step's item loads instead.
     constexpr int SLOTS = (NB - 1) * NB;
     constexpr int NREAD = 2 * NB;
-    constexpr int SCALE_SLOT = SLOTS > NREAD ? NREAD + 1 : SLOTS - 1;
+    constexpr int SCALE_SLOT = R::SCALES ? 0 : (SLOTS > NREAD ? NREAD + 1 : SLOTS - 1);
     auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
                      v8i* nbf) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
@@ -636,13 +641,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
             // reads in order of first use: row block 0 of B, the NB of A, then the rest of B
             if constexpr (!LAST) {
+                if (R::SCALES && k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
 #pragma unroll
                 for (int e = share_lo(k, NREAD, SLOTS); e < share_hi(k, NREAD, SLOTS); ++e) {
                     if (e == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
                     else if (e <= NB) na[e - 1] = frag(sa_off, frag_a, hn, e - 1);
                     else nbf[e - NB] = frag(sb_off, frag_b, hn, e - NB);
                 }
-                if (k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+                if (!R::SCALES && k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
