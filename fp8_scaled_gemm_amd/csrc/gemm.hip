@@ -38,7 +38,7 @@
 // at twice the rate of 64-byte pieces of rows (measured: 66 vs 33 bytes per
 // clock per CU from L2 for rows 8 KB apart).  Each operand of a stage (256 rows
 // x 128 B = 32 KB) is one "item" in a ring of NSLOT LDS slots (5 x 32 KB =
-// 160 KB; mode (b) with whole scale dwords uses 4 slots of 33 KB).  One item
+// 160 KB; mode (b) with whole scale dwords uses 4 slots, beside its scales).  One item
 // is loaded per K step, its 8 loads spread over that step's matrix-core
 // instructions, NSLOT-1 items ahead.  The compiler cannot track these loads
 // (it would wait for all of them before every LDS read), so they are issued
@@ -100,32 +100,37 @@ struct Geo {
     static constexpr int WT = TILE / 2;                        // wave tile edge
     static constexpr int NB = WT / 32;                         // blocks per wave-tile edge: 4 or 2
     static constexpr int OP_BYTES = TILE * BK;                 // one operand of one stage (an "item"): 32 or 16 KB
-    static constexpr int SCALE_BYTES = TILE * 4;               // mode (b): the stage's 4 block scales of every row
     static constexpr int DMA_PER_ITEM = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 8 or 4
 };
 
 // Ring geometry per kernel variant.  256-row items: 5 slots of 32 KB fill the
-// LDS, so mode (b) with whole scale dwords (each item's scales beside it)
-// fits only 4 slots of 33 KB.  128-row items: 5 slots of 16 (16.5) KB.
+// LDS, so mode (b) with whole scale dwords (scale groups beside the ring)
+// fits only 4 slots.  128-row items: 5 slots of 16 KB.
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
     using G = Geo<TILE>;
     static constexpr bool SCALES = MX && !KTAIL;
     static constexpr int NSLOT = (SCALES && TILE == 256) ? 4 : 5;
-    static constexpr int SLOT = G::OP_BYTES + (SCALES ? G::SCALE_BYTES : 0);
+    static constexpr int SLOT = G::OP_BYTES;
     static constexpr int LDS = NSLOT * SLOT;
-    static constexpr int LOADS = G::DMA_PER_ITEM + (SCALES ? 1 : 0);   // load instructions per item and wave
+    static constexpr int LOADS = G::DMA_PER_ITEM;   // load instructions per item and wave
     // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
     // slots are free (its step 1), so both its items are issued in that step
     // (none in step 0) to give them the longest lead.  5 slots: one item per
     // step, four items ahead.
     static constexpr bool PAIRED = NSLOT == 4;
-    // bf16 epilogue staging (16 KB, and the tile's sa, sb at +16 KB): with 5
-    // slots of 32 KB the slot that is free during the epilogue is borrowed;
-    // otherwise (paired, or 16 KB slots) a region after the ring is used
+    // mode (b) scale groups after the ring: 2 buffers x 2 operands x TILE rows
+    // x 16 bytes (the scales of SC_GROUP stages)
+    static constexpr int SC_GROUP = 4;
+    static constexpr int SC_AREA = LDS;
+    static constexpr int SC_OPER = TILE * 16;
+    static constexpr int SC_BYTES = SCALES ? 4 * SC_OPER : 0;
+    // bf16 epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
+    // +16 KB): with 5 slots of 32 KB the slot that is free during the epilogue
+    // is borrowed; otherwise (paired, or 16 KB slots) a region of its own
     static constexpr bool OWN_STAGE = PAIRED || TILE != 256;
-    static constexpr int STAGE_AREA = LDS;
-    static constexpr int LDS_TOTAL = LDS + (OWN_STAGE ? 18 * 1024 : 0);
+    static constexpr int STAGE_AREA = LDS + SC_BYTES;
+    static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0);
 };
 static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
                   Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024, "LDS");
@@ -231,41 +236,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // holds logical chunk (L%8) ^ ((row >> 1) & 7) = (L%8) ^ ((4w + L/16) & 7)
     const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
     const uint32_t dma_voff = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)K + dma_chunk * 16u;
-    // mode (b) scales: dword loads, lane L of wave w fills row 64w + L; with
-    // 128-row items waves 2, 3 repeat the loads of waves 0, 1 (same bytes to the
-    // same place), so that every wave issues the same number of loads per item
-    constexpr int SW = TILE / 64;   // waves with distinct scale rows
-    const uint32_t sdma_voff = (uint32_t)(64 * (wave % SW) + lane) * (uint32_t)nblk;
     constexpr uint32_t OOB_OFF = 0x80000000u;   // past any panel (panels are < 2^31 bytes)
     int ij = 0, is = 0, iop = 0, ii = 0, islot = 0;   // cursor: tile, stage in tile, operand, item, its slot
-    __amdgpu_buffer_rsrc_t rsA, rsB, rsEA, rsEB;
+    __amdgpu_buffer_rsrc_t rsA, rsB;
     auto cursor_tile = [&]() __attribute__((always_inline)) {
         const TileCoord tc = tile_of(min(ij, my_tiles - 1));
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_b = (uint32_t)min(BN, N - n0);
         rsA = panel(A + (int64_t)m0 * K, rows_a * (uint32_t)K);
         rsB = panel(B + (int64_t)n0 * K, rows_b * (uint32_t)K);
-        if constexpr (MX) {
-            rsEA = panel(ea + (int64_t)m0 * nblk, rows_a * (uint32_t)nblk);
-            rsEB = panel(eb + (int64_t)n0 * nblk, rows_b * (uint32_t)nblk);
-        }
     };
     // load q (0..LI-1) of the cursor's item
     auto dma_item = [&](int q) __attribute__((always_inline)) {
         const int s_ld = (ii < 2 * NS) ? is : nk - 1;   // past the end: reload the last stage
         const uint32_t sbuf = lds0 + (uint32_t)(islot * SLOT);
         const uint32_t k0 = (uint32_t)(s_ld * BK);
-        if (q < DMA_PER_ITEM) {
-            uint32_t voff = dma_voff;
-            if constexpr (KTAIL) {
-                // bytes past K (the next row's, or past the panel) must read as 0
-                if (k0 + dma_chunk * 16u >= (uint32_t)K) voff = OOB_OFF;
-            }
-            const uint32_t so = uniform(k0 + (uint32_t)(32 * q) * (uint32_t)K);
-            dma16(uniform(sbuf + (uint32_t)((4 * q + wave) * 1024)), voff, iop ? rsB : rsA, so);
-        } else if constexpr (R::SCALES) {
-            dma4(uniform(sbuf + (uint32_t)(OP_BYTES + (wave % SW) * 256)), sdma_voff, iop ? rsEB : rsEA,
-                 uniform((uint32_t)(4 * s_ld)));
+        uint32_t voff = dma_voff;
+        if constexpr (KTAIL) {
+            // bytes past K (the next row's, or past the panel) must read as 0
+            if (k0 + dma_chunk * 16u >= (uint32_t)K) voff = OOB_OFF;
+        }
+        const uint32_t so = uniform(k0 + (uint32_t)(32 * q) * (uint32_t)K);
+        dma16(uniform(sbuf + (uint32_t)((4 * q + wave) * 1024)), voff, iop ? rsB : rsA, so);
+    };
+
+    // ---- mode (b) scale groups (whole scale dwords, K % 128 == 0).  Group gi
+    // of a tile covers its stages 4gi .. 4gi+3: bytes 16gi .. 16gi+15 of every
+    // scale row.  Stream group number u (tile j: u = j * ngt + gi) goes to
+    // buffer u & 1, operand o at SC_AREA + (2 (u & 1) + o) * TILE * 16: row r
+    // in the 16 bytes at 16 r, the dword of group stage t at position
+    // (t + (r >> 3)) & 3 (rotated so that the 32 rows of one scale read fall in
+    // distinct banks).  Load p of an operand fills rows 16p .. 16p+15, lane L
+    // row 16p + L/4 at position L % 4: 16 bytes of a row in one or two lines,
+    // where loading each stage's dword alone touches a line per row per stage.
+    // Wave w issues loads p = w, w+4, ... of both operands.
+    constexpr int SC_LOADS = R::SCALES ? 2 * (TILE / 16) / 4 : 0;   // per wave and group: 8 or 4
+    const int ngt = (nk + R::SC_GROUP - 1) / R::SC_GROUP;            // groups per tile
+    const uint32_t sc_voff = (uint32_t)(16 * wave + (lane >> 2)) * (uint32_t)nblk +
+                             4u * (((uint32_t)(lane & 3) - (uint32_t)(2 * wave + (lane >> 5))) & 3u);
+    __amdgpu_buffer_rsrc_t rsEA, rsEB;   // scale panels of the tile of the group loaded last
+    auto sc_tile = [&](int j) __attribute__((always_inline)) {
+        const TileCoord tc = tile_of(j);
+        const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+        rsEA = panel(ea + (int64_t)m0 * nblk, (uint32_t)min(BM, M - m0) * (uint32_t)nblk);
+        rsEB = panel(eb + (int64_t)n0 * nblk, (uint32_t)min(BN, N - n0) * (uint32_t)nblk);
+    };
+    // load q (0 .. SC_LOADS-1) of group gi (of the tile of rsEA, rsEB) into buffer ub
+    auto sc_load = [&](int q, int gi, int ub) __attribute__((always_inline)) {
+        if constexpr (R::SCALES) {
+            constexpr int PER_OP = SC_LOADS / 2;
+            const int o = q / PER_OP, p = wave + 4 * (q % PER_OP);
+            const uint32_t dst = lds0 + (uint32_t)(R::SC_AREA + (2 * ub + o) * R::SC_OPER + 256 * p);
+            dma4(uniform(dst), sc_voff, o ? rsEB : rsEA,
+                 uniform((uint32_t)(16 * gi) + (uint32_t)(64 * (q % PER_OP)) * (uint32_t)nblk));
         }
     };
     auto advance = [&]() __attribute__((always_inline)) {
@@ -298,30 +321,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         return (slot + k >= NSLOT) ? slot + k - NSLOT : slot + k;
     };
 
-    // ---- mode (b) scales for step h of stream stage g: per lane and row block,
-    // the scale byte of this lane half's block in byte 0 (the matrix core reads
-    // byte 0).  With whole scale dwords: the dword of the stage (blocks 4s..4s+3)
-    // sits beside each item in LDS.  Otherwise (rows of nblk bytes, not a
-    // multiple of 4): unconditional byte loads from global, 2^0 past the row
-    // end; rows past M / N read 0 (their data is zero too).
-    auto read_scales = [&](int g, int h, uint32_t sa_off, uint32_t sb_off, uint32_t* xa, uint32_t* xb)
-                           __attribute__((always_inline)) {
+    // ---- mode (b) scales for step h of stage s of stream tile j: per lane and
+    // row block, the scale byte of this lane half's block in byte 0 (the matrix
+    // core reads byte 0).  With whole scale dwords: the stage's dword (blocks
+    // 4s .. 4s+3) from the LDS scale group.  Otherwise (rows of nblk bytes, not
+    // a multiple of 4): unconditional byte loads from global, 2^0 past the row
+    // end; rows past M / N read 0 (their data is zero too).  j < my_tiles.
+    auto read_scales = [&](int j, int s, int h, uint32_t* xa, uint32_t* xb) __attribute__((always_inline)) {
         if constexpr (MX) {
             if constexpr (R::SCALES) {
                 const uint32_t sh = (uint32_t)(8 * (2 * h + lhi));
-                const uint8_t* sca = smem + sa_off + OP_BYTES;
-                const uint8_t* scb = smem + sb_off + OP_BYTES;
+                const int ub = (j * ngt + s / R::SC_GROUP) & 1;
+                const uint8_t* sca = smem + R::SC_AREA + 2 * ub * R::SC_OPER;
+                const uint8_t* scb = sca + R::SC_OPER;
+                // row wm*WT + 32i + l32: (row >> 3) & 3 == (l32 >> 3) & 3
+                const uint32_t pos = (((uint32_t)(s & 3) + (uint32_t)(l32 >> 3)) & 3u) * 4u;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32) * 4) >> sh;
-                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32) * 4) >> sh;
+                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32) * 16 + pos) >> sh;
+                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32) * 16 + pos) >> sh;
                 }
             } else {
-                const TileCoord tc = tile_of(g / nk);
+                const TileCoord tc = tile_of(j);
                 const int m0 = tc.tm * BM, n0 = tc.tn * BN;
                 const __amdgpu_buffer_rsrc_t pa = panel(ea + (int64_t)m0 * nblk, (uint32_t)min(BM, M - m0) * (uint32_t)nblk);
                 const __amdgpu_buffer_rsrc_t pb = panel(eb + (int64_t)n0 * nblk, (uint32_t)min(BN, N - n0) * (uint32_t)nblk);
-                const int kb = 4 * (g % nk) + 2 * h + lhi;   // this lane half's block
+                const int kb = 4 * s + 2 * h + lhi;   // this lane half's block
                 const bool in = kb < nblk;
                 const uint32_t kc = (uint32_t)min(kb, nblk - 1);
 #pragma unroll
@@ -552,9 +577,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     }
     if (NS == 0) return;
 
-    // ---- prologue: items 0 .. NSLOT-2 in flight; stage 0 (items 0, 1) landed
-    // and the fragments of its step 0 read
+    // ---- prologue: items 0 .. NSLOT-2 in flight; stage 0 (items 0, 1) and the
+    // first scale group (loaded before them) landed, and the fragments and
+    // scales of step 0 read
     cursor_tile();
+    if constexpr (R::SCALES) {
+        sc_tile(0);
+#pragma unroll
+        for (int q = 0; q < SC_LOADS; ++q) sc_load(q, 0, 0);
+    }
     constexpr int PRO_ITEMS = R::PAIRED ? 4 : NSLOT - 1;   // items in flight before step 0
     for (int i = 0; i < PRO_ITEMS; ++i) {
 #pragma unroll
@@ -573,15 +604,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         fa0[i] = frag(0, frag_a, 0, i);
         fb0[i] = frag(SLOT, frag_b, 0, i);
     }
-    read_scales(0, 0, 0, SLOT, xa, xb);
+    read_scales(0, 0, 0, xa, xb);
     int rslot = 0;   // LDS slot of the current stage's A item (its B item is the next slot)
 
-    // ---- one K step: step h of stream stage g (fragments and scales in registers).
+    // ---- one K step: step h of stage s of stream tile j (fragments and scales
+    // in registers).
     //   the 4 matrix-core steps of row block 0;
-    //   h == 1 only: wait until stage g+1's items landed (items past them may be
-    //   in flight) and sync: they landed for every wave, and every wave's reads
-    //   of stage g's items (done during step 0) are finished (the barrier waits
-    //   for outstanding LDS reads), so their slots may be refilled;
+    //   h == 1 only: wait until the next stage's items landed (items past them
+    //   may be in flight) and sync: they landed for every wave, and every wave's
+    //   reads of this stage's items (done during step 0) are finished (the
+    //   barrier waits for outstanding LDS reads), so their slots may be refilled;
     //   12 slots, each one matrix-core step plus one load of the item NSLOT-1
     //   ahead (into the slot of the item just before this step's) and two
     //   16-byte LDS reads of the next step's fragments into the other register
@@ -596,17 +628,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // first matrix-core instruction until every fragment read had landed.
     // Scales loaded byte-wise from global memory (K tail) are read after the
     // step's item loads instead.
+    // Mode (b) scale groups: step 0 of a group's first stage loads the next
+    // group (the tile's next, or the next tile's first) into the other buffer,
+    // whose group was last read in step 0 of the stage before, ahead of the
+    // barrier of that stage's step 1.  The paired ring spreads the loads over
+    // this step, which loads no items; with 5 slots they go first, before the
+    // item loads, which the next wait may leave in flight.  Either way they
+    // have landed at that wait, the earliest point the group is read.
     constexpr int SLOTS = (NB - 1) * NB;
     constexpr int NREAD = 2 * NB;
     constexpr int SCALE_SLOT = R::SCALES ? 0 : (SLOTS > NREAD ? NREAD + 1 : SLOTS - 1);
-    auto kstep = [&](v16f (&acc)[NB][NB], int g, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
+    auto kstep = [&](v16f (&acc)[NB][NB], int j, int s, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
                      v8i* nbf) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
+        bool sc_go = false;
+        int sc_gi = 0, sc_ub = 0;
+        if constexpr (R::SCALES) {
+            if (h == 0 && s % R::SC_GROUP == 0) {
+                const bool in_tile = s + R::SC_GROUP < nk;
+                if (in_tile || j + 1 < my_tiles) {
+                    if (!in_tile) sc_tile(j + 1);
+                    sc_go = true;
+                    sc_gi = in_tile ? s / R::SC_GROUP + 1 : 0;
+                    sc_ub = (j * ngt + s / R::SC_GROUP + 1) & 1;
+                }
+            }
+        }
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
-            // stage g+1's items landed: with 5 slots one later item may be in
+            // the next stage's items landed: with 5 slots one later item may be in
             // flight; with 4 (paired) none
             wait_vmcnt<(R::PAIRED ? 0 : NSLOT - 4) * LI>();
             __syncthreads();
@@ -616,11 +668,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             // all but those leaves the scales landed)
             if constexpr (!MX && LAST) {
                 if (staged)
-                    tile_scales_to_lds(g / nk, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
+                    tile_scales_to_lds(j, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        const int gn = h ? g + 1 : g, hn = h ^ 1;
+        const int sn = h ? s + 1 : s, hn = h ^ 1;
         const int na_slot = h ? slot_add(rslot, 2) : rslot;   // slots of the items read next
         const uint32_t sa_off = (uint32_t)(na_slot * SLOT), sb_off = (uint32_t)(slot_add(na_slot, 1) * SLOT);
         uint32_t nxa[NB], nxb[NB];
@@ -628,6 +680,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int k = 0; k < SLOTS; ++k) {
             const int i = 1 + k / NB, jb = k % NB;
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
+            if constexpr (R::SCALES) {
+                if (sc_go) {
+                    if constexpr (R::PAIRED) {
+#pragma unroll
+                        for (int q = share_lo(k, SC_LOADS, SLOTS); q < share_hi(k, SC_LOADS, SLOTS); ++q)
+                            sc_load(q, sc_gi, sc_ub);
+                    } else if (k == 0) {
+#pragma unroll
+                        for (int q = 0; q < SC_LOADS; ++q) sc_load(q, sc_gi, sc_ub);
+                    }
+                }
+            }
             if constexpr (!R::PAIRED) {
 #pragma unroll
                 for (int q = share_lo(k, LI, SLOTS); q < share_hi(k, LI, SLOTS); ++q) dma_item(q);
@@ -641,14 +705,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
             // reads in order of first use: row block 0 of B, the NB of A, then the rest of B
             if constexpr (!LAST) {
-                if (R::SCALES && k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+                if (R::SCALES && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
 #pragma unroll
                 for (int e = share_lo(k, NREAD, SLOTS); e < share_hi(k, NREAD, SLOTS); ++e) {
                     if (e == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
                     else if (e <= NB) na[e - 1] = frag(sa_off, frag_a, hn, e - 1);
                     else nbf[e - NB] = frag(sb_off, frag_b, hn, e - NB);
                 }
-                if (!R::SCALES && k == SCALE_SLOT) read_scales(gn, hn, sa_off, sb_off, nxa, nxb);
+                if (!R::SCALES && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -668,20 +732,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     using NotLast = std::integral_constant<bool, false>;
     using Last = std::integral_constant<bool, true>;
 
-    int g = 0;
     for (int j = 0; j < my_tiles; ++j) {
         v16f acc[NB][NB];   // [n block][m block]
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-        for (int s = 0; s < nk - 1; ++s, ++g) {
-            kstep(acc, g, 0, NotLast{}, fa0, fb0, fa1, fb1);
-            kstep(acc, g, 1, NotLast{}, fa1, fb1, fa0, fb0);
+        for (int s = 0; s < nk - 1; ++s) {
+            kstep(acc, j, s, 0, NotLast{}, fa0, fb0, fa1, fb1);
+            kstep(acc, j, s, 1, NotLast{}, fa1, fb1, fa0, fb0);
         }
-        kstep(acc, g, 0, NotLast{}, fa0, fb0, fa1, fb1);
-        kstep(acc, g, 1, Last{}, fa1, fb1, fa0, fb0);
-        ++g;
+        kstep(acc, j, nk - 1, 0, NotLast{}, fa0, fb0, fa1, fb1);
+        kstep(acc, j, nk - 1, 1, Last{}, fa1, fb1, fa0, fb0);
         if (staged) {
             // the slot of the last stage's B item is free until the next K step
             // loads into it (every wave finished reading it before the last barrier)
@@ -694,13 +756,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         }
         // the next stage's step-0 fragments and scales (its items landed before
         // the last barrier; the slots of this stage's items are not refilled
-        // before the next barrier)
+        // before the next barrier).  After the last tile the fragment reads
+        // (LDS) are harmless and unused; the scales are read only for a tile
+        // that exists (the K-tail path reads them from global memory).
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             fa0[i] = frag((uint32_t)(rslot * SLOT), frag_a, 0, i);
             fb0[i] = frag((uint32_t)(slot_add(rslot, 1) * SLOT), frag_b, 0, i);
         }
-        read_scales(g, 0, (uint32_t)(rslot * SLOT), (uint32_t)(slot_add(rslot, 1) * SLOT), xa, xb);
+        if (j + 1 < my_tiles) read_scales(j + 1, 0, 0, xa, xb);
     }
     wait_vmcnt<0>();   // the past-the-end loads must land before the workgroup exits
 }

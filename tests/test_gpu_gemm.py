@@ -262,3 +262,28 @@ def test_mode_b_mx_workload(gpu_lib):
     W = gemm.mxfp8_gemm_weight(qa[sm], qb[sn], ea[sm], eb[sn])
     assert_gemm_close(to_host(D)[np.ix_(sm, sn)], ref, W, "bf16", w.name,
                       gemm.alignment_term(qa[sm], qb[sn], ea=ea[sm], eb=eb[sn]))
+
+
+# Whole scale dwords (K % 128 == 0): the scales of 4 stages at a time are
+# staged together, so the last group of a tile is partial unless the stages
+# per tile (K / 128) are a multiple of 4, and with more tiles than workgroups
+# a workgroup's next tile's first group is loaded during its current tile.
+# 4352 x 4096: 272 tiles of 256 for 256 workgroups; 2048 x 4096: 128 tiles of
+# 256, so 512 tiles of 128 (two per workgroup).  Rows and columns sampled at
+# a stride cover every tile.
+SHAPES_B_GROUPS = [(4352, 4096, 128), (4352, 4096, 384), (4352, 4096, 640), (4352, 4096, 1664),
+                   (2048, 4096, 640), (2048, 4096, 896)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES_B_GROUPS)
+def test_mode_b_scale_groups(gpu_lib, M, N, K):
+    seed = M + 7 * N + 3 * K
+    A, B = codes(seed, (M, K)), codes(seed, (N, K), 2)
+    ea, eb = mx_scales(seed, M, K // 32, 7), mx_scales(seed, N, K // 32, 8)
+    say("mode b scale groups", M, N, K)
+    D = gpu_mx(gpu_lib, A, B, ea, eb, "bf16")
+    sm = np.union1d(np.arange(0, M, 13), [M - 1])
+    sn = np.union1d(np.arange(0, N, 11), [N - 1])
+    assert_gemm_close(D[np.ix_(sm, sn)], gemm.mxfp8_gemm(A[sm], B[sn], ea[sm], eb[sn]),
+                      gemm.mxfp8_gemm_weight(A[sm], B[sn], ea[sm], eb[sn]), "bf16",
+                      "mode b groups %dx%dx%d" % (M, N, K), gemm.alignment_term(A[sm], B[sn], ea=ea[sm], eb=eb[sn]))
