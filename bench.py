@@ -50,11 +50,22 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# Default step counts.  After the GPU has been idle (inputs are drawn on the
+# host first) its clock takes some 25-40 ms of work to ramp up: the FFN-up
+# GEMM runs at about 1.36 ms per launch at first and holds 1.03 ms from about
+# 40 ms on, for at least a second.  So the warmup covers about 100 ms of work
+# and the timed steps about 60 ms (per mode for the quantize workload).
+DEFAULT_WARMUP = {"ffn_up": 80, "mx": 300, "concat_mla": 1000, "quantize": 1000}
+DEFAULT_STEPS = {"ffn_up": 50, "mx": 200, "concat_mla": 500, "quantize": 500}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default: about 60 ms of GPU work for the workload)")
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps first (default: about 100 ms of GPU work for the workload)")
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up",
                    help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k; "
                         "quantize: every fp8_quantize_ex mode on the FFN-up activations")
@@ -69,7 +80,12 @@ def parse():
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run a plain device-to-device copy of this many bytes (calibrates the "
                         "HBM byte counters of a profiler run against a known size)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS[args.workload]
+    if args.warmup is None:
+        args.warmup = DEFAULT_WARMUP[args.workload]
+    return args
 
 
 def copy_only(nbytes, reps=5):
