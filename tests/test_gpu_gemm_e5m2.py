@@ -141,7 +141,9 @@ def test_ex_dtype_checks(gpu_lib):
         gpu_lib.fp8_gemm_scaled_ex(4, 4, 64, A.view(torch.uint8), 2, B, E5M2, s, s)
 
 
-SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160), (2600, 2900, 1024)]
+# K / 128 = 3 and 5: the last group of 4 stages' block scales is partial
+SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160), (2600, 2900, 1024),
+            (300, 260, 384), (200, 300, 640)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -180,3 +182,23 @@ def test_ex_mode_b_scale_association_e5m2(gpu_lib):
         want = np.outer(e5m2.decode(base_a) * quant.ue8m0_value(ea[:, j]),
                         e4m3.decode(base_b) * quant.ue8m0_value(eb[:, j]))
         assert np.array_equal(D, want), j
+
+
+def test_ex_mode_b_scale_groups_e5m2(gpu_lib):
+    """E5M2 x E5M2 MX at 4352 x 4096 x 640: 272 tiles of 256 for 256
+    workgroups, 5 stages per tile (a partial last group of 4 stages' block
+    scales, and groups loaded for a workgroup's next tile); rows and columns
+    sampled at a stride cover every tile."""
+    M, N, K = 4352, 4096, 640
+    seed = 99
+    A, B = finite_codes(seed, (M, K), E5M2), finite_codes(seed, (N, K), E5M2, 2)
+    ea = (synth.u8_codes(seed, 7, (M, K // 32)) % 41 + 107).astype(np.uint8)
+    eb = (synth.u8_codes(seed, 8, (N, K // 32)) % 41 + 107).astype(np.uint8)
+    say("ex mode b scale groups e5m2", M, N, K)
+    D = gpu_mx_ex(gpu_lib, A, E5M2, B, E5M2, ea, eb, "bf16")
+    sm = np.union1d(np.arange(0, M, 13), [M - 1])
+    sn = np.union1d(np.arange(0, N, 11), [N - 1])
+    a, b, sa_, sb_ = A[sm], B[sn], ea[sm], eb[sn]
+    assert_gemm_close(D[np.ix_(sm, sn)], gemm.mxfp8_gemm(a, b, sa_, sb_, "e5m2", "e5m2"),
+                      gemm.mxfp8_gemm_weight(a, b, sa_, sb_, "e5m2", "e5m2"), "bf16", "ex mode b groups e5m2",
+                      gemm.alignment_term(a, b, ea=sa_, eb=sb_, fmt_a="e5m2", fmt_b="e5m2"))
