@@ -55,6 +55,8 @@ def log(*a):
 # GEMM runs at about 1.36 ms per launch at first and holds 1.03 ms from about
 # 40 ms on, for at least a second.  So the warmup covers about 100 ms of work
 # and the timed steps about 60 ms (per mode for the quantize workload).
+CONCAT_SETS = 2    # rotating buffer sets for the concat_mla workload
+QUANT_SETS = 4     # rotating buffer sets for the quantize workload
 DEFAULT_WARMUP = {"ffn_up": 80, "mx": 300, "concat_mla": 1000, "quantize": 1000}
 DEFAULT_STEPS = {"ffn_up": 50, "mx": 200, "concat_mla": 500, "quantize": 500}
 
@@ -199,17 +201,20 @@ def concat_bench(args, torch, fp8g):
     bits = synth.raw_u64(synth.stream_key(0xC0C0A7, 2), 0, T * 64 // 8)
     rope = torch.from_numpy(bits.view(np.uint8).reshape(T, 1, 64)).to(dev).view(torch.float8_e4m3fn)
     k = torch.empty((T, H, 192), dtype=torch.float8_e4m3fn, device=dev)
+    # calls rotate over CONCAT_SETS distinct buffer sets (671 MB each), so that
+    # the 256 MB infinity cache cannot serve one call's data to the next
+    sets = [(nope, rope, k)] + [(nope.clone(), rope.clone(), torch.empty_like(k)) for _ in range(CONCAT_SETS - 1)]
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        fp8g.concat_mla_k(nope, rope, k)
+    for i in range(args.warmup):
+        fp8g.concat_mla_k(*sets[i % CONCAT_SETS])
     torch.cuda.synchronize()
     # one event pair around the back-to-back launches on the stream (a pair per
     # 100 us launch would add its own few us)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        fp8g.concat_mla_k(nope, rope, k)
+    for i in range(args.steps):
+        fp8g.concat_mla_k(*sets[i % CONCAT_SETS])
     e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -221,7 +226,8 @@ def concat_bench(args, torch, fp8g):
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "u8", "data": "synthetic",
             "config": {"workload": WORKLOADS["concat_mla"], "tokens": T, "heads": H, "nope": 128, "rope": 64,
-                       "elem_bytes": 1, "rope_heads": 1},
+                       "elem_bytes": 1, "rope_heads": 1, "rotating_buffer_sets": CONCAT_SETS,
+                       "rotating_bytes": CONCAT_SETS * nbytes},
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                          "traffic": read_traffic(os.path.join(ROOT, TRAFFIC_FILES["concat_mla"]), "concat.hip"),
@@ -257,29 +263,34 @@ def quantize_bench(args, torch, fp8g):
     w = synth.WORKLOADS[WORKLOADS["quantize"]]
     dev = torch.device("cuda", 0)
     X = torch.from_numpy(synth.draw(w, "a")).to(dev)
-    Xb = X.to(torch.bfloat16)
     R, C = X.shape
-    q = torch.empty((R, C), dtype=torch.uint8, device=dev)
-    s_row = torch.empty((R,), dtype=torch.float32, device=dev)
-    s_ten = torch.empty((1,), dtype=torch.float32, device=dev)
+    # calls rotate over QUANT_SETS distinct inputs and outputs (1.3 GB for fp32
+    # input), so that the 256 MB infinity cache cannot serve one call's data
+    # to the next
+    Xs = [X] + [X.clone() for _ in range(QUANT_SETS - 1)]
+    Xbs = [x.to(torch.bfloat16) for x in Xs]
+    qs = [torch.empty((R, C), dtype=torch.uint8, device=dev) for _ in range(QUANT_SETS)]
+    s_rows = [torch.empty((R,), dtype=torch.float32, device=dev) for _ in range(QUANT_SETS)]
+    s_tens = [torch.empty((1,), dtype=torch.float32, device=dev) for _ in range(QUANT_SETS)]
     stream = torch.cuda.current_stream()
     res = {}
     for name, bf, pt, fmt in QUANT_MODES:
-        x = Xb if bf else X
-        sc = s_ten if pt else s_row
+        xs = Xbs if bf else Xs
+        scs = s_tens if pt else s_rows
 
-        def call():
-            fp8g.fp8_quantize_ex(x, per_tensor=pt, q=q, scale=sc, fmt=fmt)
-        for _ in range(args.warmup):
-            call()
+        def call(i):
+            j = i % QUANT_SETS
+            fp8g.fp8_quantize_ex(xs[j], per_tensor=pt, q=qs[j], scale=scs[j], fmt=fmt)
+        for i in range(args.warmup):
+            call(i)
         torch.cuda.synchronize()
         # one event pair around the back-to-back launches on the stream: a pair
         # per launch of a 50 us kernel adds several us of its own
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
-        for _ in range(args.steps):
-            call()
+        for i in range(args.steps):
+            call(i)
         e1.record(stream)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
@@ -292,7 +303,8 @@ def quantize_bench(args, torch, fp8g):
             "value": round(head["bytes"] / (head["ms_per_call"] * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_call"], 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "quantize_ffn_up_activations_8192x8192", "rows": R, "cols": C},
+            "config": {"workload": "quantize_ffn_up_activations_8192x8192", "rows": R, "cols": C,
+                       "rotating_buffer_sets": QUANT_SETS, "rotating_bytes": QUANT_SETS * head["bytes"]},
             "roofline": {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(head["gbs"] / PEAK_HBM_GBS, 4),
                          "traffic": read_traffic(os.path.join(ROOT, TRAFFIC_FILES["quantize"]), "quantize.hip"),
@@ -415,6 +427,8 @@ def main():
     elapsed = time.perf_counter() - t0
     per_kernel = {k: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
                   for j, k in enumerate(kernels)}      # microseconds
+    per_kernel_median = {k: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e3
+                         for j, k in enumerate(kernels)}
 
     ms_per_step = elapsed / args.steps * 1e3
     flops = float(w.flops)
@@ -439,9 +453,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "N": N, "K": K, "out": "bf16",
                    "mode": "per-token x per-channel scales" if w.mode == "a" else "MXFP8",
-                   "step": " -> ".join(kernels), "fmt_a": args.fmt_a, "fmt_b": args.fmt_b},
+                   "step": " -> ".join(kernels), "fmt_a": args.fmt_a, "fmt_b": args.fmt_b,
+                   "cache": "hot: the GEMM reads the codes the step's quantizers have just written"},
         "pct_of_fp8_peak_step": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
+        "kernels_us_median": {k: round(v, 2) for k, v in per_kernel_median.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
                      "kernel": "gemm_fp8_kernel", "flops_per_launch": flops},
