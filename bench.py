@@ -330,7 +330,7 @@ def quantize_bench(args, torch, fp8g):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -172,7 +172,7 @@ const char* fp8g_status_string(int status) {
         case FP8G_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case FP8G_ERR_DTYPE: return "unknown output dtype, operand format, input dtype, granularity or element size";
         case FP8G_ERR_OVERLAP: return "an output overlaps an input or another output";
-        case FP8G_ERR_UNSUPPORTED: return "outside this build's limits (GEMM: k % 16, k >= 2^23, m >= 2^31, a 256-row panel of D over 2^31 bytes; quantizer rows >= 2^31; size overflow)";
+        case FP8G_ERR_UNSUPPORTED: return "outside the library's limits (GEMM: k % 16, k >= 2^23, m >= 2^31, a 256-row panel of D over 2^31 bytes; quantizer rows >= 2^31; size overflow)";
         case FP8G_ERR_HIP: return "the HIP runtime rejected the launch";
         default: return "unknown status";
     }

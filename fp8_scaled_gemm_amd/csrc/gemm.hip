@@ -170,6 +170,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The lane index, computed afresh (v_mbcnt) inside an opaque statement.  Code
+// that runs once per tile (epilogues, the tile's scale loads) derives its
+// lane-dependent values from this rather than from the kernel's own lane index:
+// the compiler then cannot hoist them to the kernel start, where they would
+// stay live through the main loop and be spilled.  Each spill reload is a
+// scratch load, and the compiler waits for it with a count that does not know
+// about the operand loads issued from inline assembly, so it waited for all of
+// them too (measured: two such waits per tile).
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 struct TileCoord {
     int tm, tn;
 };
@@ -389,6 +403,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const __amdgpu_buffer_rsrc_t rsD =
             panel(reinterpret_cast<uint8_t*>(Dv) + (int64_t)m0 * N * ESZ, rows * (uint32_t)N * ESZ);
         constexpr uint32_t OOB = 0x80000000u;   // beyond any panel (panels are < 2^31 bytes)
+        const int lane_u = fresh_lane();
+        const int l32 = lane_u & 31, lhi = lane_u >> 5;
         float smv[NB], snv[NB][4][4];
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
@@ -473,7 +489,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         if constexpr (!MX) {
             const TileCoord tc = tile_of(j);
             const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-            const uint32_t v = (uint32_t)(64 * wave + lane) * 4u;   // lane L of wave w: element 64w + L
+            const uint32_t v = (uint32_t)(64 * wave + fresh_lane()) * 4u;   // lane L of wave w: element 64w + L
             dma4(uniform(lds0 + stage_off + SC_OFF + (uint32_t)(wave * 256)), v,
                  panel(sa + m0, (uint32_t)min(BM, M - m0) * 4u), 0u);
             dma4(uniform(lds0 + stage_off + SC_OFF + 1024u + (uint32_t)(wave * 256)), v,
@@ -487,11 +503,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const __amdgpu_buffer_rsrc_t rsD =
             panel(reinterpret_cast<uint8_t*>(Dv) + (int64_t)m0 * N * 2, rows * (uint32_t)N * 2u);
         constexpr uint32_t OOB = 0x80000000u;
-        // lane-derived values are computed here from an opaque copy of the lane
-        // index: hoisted to the kernel start they would stay live through the
-        // main loop and be spilled, and each reload would wait for the stores
-        int lane_e = lane;
-        asm volatile("" : "+v"(lane_e));
+        const int lane_e = fresh_lane();
         const int l32e = lane_e & 31, lhie = lane_e >> 5;
         uint8_t* st = smem + stage_off + wave * 4096;
         const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);

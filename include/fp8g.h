@@ -71,7 +71,7 @@ typedef enum {
     FP8G_ERR_ALIGN = 3,       /* pointer not 16-byte aligned */
     FP8G_ERR_DTYPE = 4,       /* unknown out_dtype, operand format, input dtype, granularity or element size */
     FP8G_ERR_OVERLAP = 5,     /* an output overlaps an input or another output */
-    FP8G_ERR_UNSUPPORTED = 6, /* valid but outside this build's limits (see each call) */
+    FP8G_ERR_UNSUPPORTED = 6, /* valid but outside the library's limits (see each call) */
     FP8G_ERR_HIP = 7          /* the HIP runtime refused the launch */
 } fp8g_status_t;
 

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library and a CUDA device, or a hard failure on a GPU machine."""
+    """The HIP library and a CUDA device, or a hard failure on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU in this container")
