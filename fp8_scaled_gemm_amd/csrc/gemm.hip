@@ -141,6 +141,15 @@ __host__ __device__ constexpr int share_lo(int k, int n, int s) { return s >= n 
 __host__ __device__ constexpr int share_hi(int k, int n, int s) { return s >= n ? (k < n ? k + 1 : n) : (k + 1) * n / s; }
 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
+// Cache policy of the staged epilogue's D stores (whole 128-byte lines):
+// non-temporal.  Every workgroup writes its finished tile at about the same
+// time (4 MB per XCD for a round of 256x256 bf16 tiles, the size of the XCD's
+// L2); with the default policy that burst displaced the operand panels the
+// XCD's tiles share.  Measured at 8192x22016x8192: 1.4-2% faster
+// (write-through, sc0 sc1: no gain).  Stores of parts of lines (the epilogue
+// from registers) keep the default policy: non-temporal, they ran 30-50%
+// slower.
+constexpr int ST_NT = 2;
 
 // ---------------------------------------------------------------- helpers
 
@@ -389,14 +398,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         asm volatile("" : "+a"(c));
     };
 
-    // ---- epilogue of stream tile j: lane holds m = .. + l32 and n = .. + 8g + 4*lhi + t
-    // (t = 0..3) in acc[.][.][4g+t].  Buffer loads / stores over the tile's rows of
-    // D, sa, sb: out-of-range lanes get an offset past the end, which the hardware
-    // drops (stores) or reads as 0.  All scale loads are issued before the first
-    // store: the vector-memory counter also counts stores, so a load waited for
-    // after stores would wait for those stores too.
+    // ---- epilogue of stream tile j from registers (fp32 output, or N % 8 != 0):
+    // lane holds m = .. + l32 and n = .. + 8g + 4*lhi + t (t = 0..3) in
+    // acc[.][.][4g+t].  Stores over the tile's rows of D: out-of-range lanes get
+    // an offset past the end, which the hardware drops.  Mode (a) reads the
+    // tile's sa, sb from LDS at stage_off + 16 KB / + 17 KB (loaded by
+    // tile_scales_to_lds during the tile's last K step, like the staged
+    // epilogue): loaded here into registers, the compiler's wait for them would
+    // also wait for the next tile's operand loads in flight.
     constexpr int ESZ = OUT_F32 ? 4 : 2;
-    auto epilogue = [&](int j, v16f (&acc)[NB][NB]) __attribute__((always_inline)) {
+    constexpr uint32_t SC_OFF = 16384;   // the tile's sa at stage_off + 16 KB, sb at + 17 KB
+    auto epilogue = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
         const TileCoord tc = tile_of(j);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows = (uint32_t)min(BM, M - m0);
@@ -405,29 +417,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         constexpr uint32_t OOB = 0x80000000u;   // beyond any panel (panels are < 2^31 bytes)
         const int lane_u = fresh_lane();
         const int l32 = lane_u & 31, lhi = lane_u >> 5;
+        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
+        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
         float smv[NB], snv[NB][4][4];
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             smv[jb] = 1.0f;
-            if constexpr (!MX) {
-                const int mr = wm * WT + jb * 32 + l32;
-                smv[jb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                        panel(sa + m0, rows * 4u), m0 + mr < M ? (uint32_t)mr * 4u : OOB, 0, 0));
-            }
+            if constexpr (!MX) smv[jb] = lsa[wm * WT + jb * 32 + l32];   // rows past M hold 0 (and are not stored)
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq)
+            for (int gq = 0; gq < 4; ++gq) {
+                if constexpr (!MX) {
+                    // a float vector: __builtin_bit_cast of an element of an integer
+                    // vector reads element 0 whatever the index (clang)
+                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + i * 32 + 8 * gq + 4 * lhi);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    snv[i][gq][t] = 1.0f;
-                    if constexpr (!MX) {
-                        const int n = n0 + wn * WT + i * 32 + 8 * gq + 4 * lhi + t;
-                        snv[i][gq][t] = __builtin_bit_cast(
-                            float, __builtin_amdgcn_raw_buffer_load_b32(panel(sb, (uint32_t)N * 4u), (uint32_t)n * 4u, 0, 0));
-                    }
+                    for (int t = 0; t < 4; ++t) snv[i][gq][t] = t4[t];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) snv[i][gq][t] = 1.0f;
                 }
+            }
         __builtin_amdgcn_sched_barrier(0);
         const bool vec_ok = (N % 4) == 0;
 #pragma unroll
@@ -484,7 +496,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // chunk c of row r in physical chunk c ^ ((r >> 1) & 7), its 8-byte halves
     // swapped when r >= 16: the 8-byte writes of 32 rows and the 16-byte reads of
     // 2 rows per LDS cycle both hit distinct banks.
-    constexpr uint32_t SC_OFF = 16384;   // sa at +16 KB, sb at +17 KB
     auto tile_scales_to_lds = [&](int j, uint32_t stage_off) __attribute__((always_inline)) {
         if constexpr (!MX) {
             const TileCoord tc = tile_of(j);
@@ -561,7 +572,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     if (k >= 2) d = (v4u){d.z, d.w, d.x, d.y};   // rows 16..31: halves swapped
                     const uint32_t mr = (uint32_t)(wm * WT + jb * 32 + 8 * k + rr);   // row inside the tile
                     const uint32_t off = mr * (uint32_t)N * 2u + col_off;
-                    __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, ST_NT);
                 }
             }
         }
@@ -575,15 +586,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             for (int i = 0; i < NB; ++i)
 #pragma unroll
                 for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-            if (staged) {
-                tile_scales_to_lds(j, 0);
-                wait_vmcnt<0>();
-                __syncthreads();
-                epilogue_staged(j, acc, 0);
-                __syncthreads();
-            } else {
-                epilogue(j, acc);
-            }
+            tile_scales_to_lds(j, 0);
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (staged) epilogue_staged(j, acc, 0);
+            else epilogue(j, acc, 0);
+            __syncthreads();
         }
         return;
     }
@@ -676,11 +684,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             __syncthreads();
             // last stage of a tile: the slot of its B item is now free until the
             // next tile's first step; load the tile's scales into it for the
-            // staged epilogue (before this step's item loads, so that waiting for
-            // all but those leaves the scales landed)
+            // epilogue (before this step's item loads, so that waiting for all
+            // but those leaves the scales landed)
             if constexpr (!MX && LAST) {
-                if (staged)
-                    tile_scales_to_lds(j, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
+                tile_scales_to_lds(j, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -756,15 +763,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         }
         kstep(acc, j, nk - 1, 0, NotLast{}, fa0, fb0, fa1, fb1);
         kstep(acc, j, nk - 1, 1, Last{}, fa1, fb1, fa0, fb0);
+        // the slot of the last stage's B item is free until the next K step
+        // loads into it (every wave finished reading it before the last barrier)
+        const uint32_t stage_off = R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT);
         if (staged) {
-            // the slot of the last stage's B item is free until the next K step
-            // loads into it (every wave finished reading it before the last barrier)
             if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
-            epilogue_staged(j, acc, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT));
+            epilogue_staged(j, acc, stage_off);
             __syncthreads();   // staging reads done before that slot is loaded again
         } else {
-            epilogue(j, acc);
+            if constexpr (!MX) {
+                wait_vmcnt<LI>();
+                __syncthreads();
+            }
+            epilogue(j, acc, stage_off);
+            if constexpr (!MX) __syncthreads();   // scale reads done before that slot is loaded again
         }
         // the next stage's step-0 fragments and scales (its items landed before
         // the last barrier; the slots of this stage's items are not refilled
