@@ -141,14 +141,15 @@ __host__ __device__ constexpr int share_lo(int k, int n, int s) { return s >= n 
 __host__ __device__ constexpr int share_hi(int k, int n, int s) { return s >= n ? (k < n ? k + 1 : n) : (k + 1) * n / s; }
 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
-// Cache policy of the staged epilogue's D stores (whole 128-byte lines):
-// non-temporal.  Every workgroup writes its finished tile at about the same
-// time (4 MB per XCD for a round of 256x256 bf16 tiles, the size of the XCD's
-// L2); with the default policy that burst displaced the operand panels the
-// XCD's tiles share.  Measured at 8192x22016x8192: 1.4-2% faster
-// (write-through, sc0 sc1: no gain).  Stores of parts of lines (the epilogue
-// from registers) keep the default policy: non-temporal, they ran 30-50%
-// slower.
+// Cache policy of the staged epilogues' D stores (each store instruction
+// writes 8 rows x 128 contiguous bytes): non-temporal.  Every workgroup writes
+// its finished tile at about the same time (4 MB per XCD for a round of
+// 256x256 bf16 tiles, the size of the XCD's L2); with the default policy that
+// burst displaced the operand panels the XCD's tiles share.  Measured at
+// 8192x22016x8192: 1.4-2% faster in mode (a), 3% in mode (b); at N = 22008
+// (rows not whole lines) still 0.8% (write-through, sc0 sc1: no gain).  The
+// epilogue from registers (16 bytes or less in each of 32 rows per store)
+// keeps the default policy: non-temporal, it ran 30-50% slower.
 constexpr int ST_NT = 2;
 
 // ---------------------------------------------------------------- helpers
@@ -577,7 +578,86 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
         }
     };
-    const bool staged = !OUT_F32 && (N % 8) == 0;
+    // ---- fp32 epilogue through LDS (mode (a), N % 4 == 0): as the bf16 one, with bands of
+    // one 32x32 block (32 rows x 128 bytes, 4 KB per wave).  Lane (l32, lhi)
+    // writes the 16-byte chunks 2 gq + lhi (gq = 0..3) of band row l32, logical
+    // chunk c of row r at physical chunk c ^ ((r >> 1) & 7): the writes of 16
+    // lanes (16 rows, one chunk) and the reads of 16 lanes (2 rows, 8 chunks)
+    // both hit 16 distinct 16-byte bank groups.  Read back row-contiguously, 8
+    // lanes store one 128-byte row of the band, as whole lines.
+    auto epilogue_staged_f32 = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+        const TileCoord tc = tile_of(j);
+        const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+        const uint32_t rows = (uint32_t)min(BM, M - m0);
+        const __amdgpu_buffer_rsrc_t rsD =
+            panel(reinterpret_cast<uint8_t*>(Dv) + (int64_t)m0 * N * 4, rows * (uint32_t)N * 4u);
+        constexpr uint32_t OOB = 0x80000000u;
+        const int lane_e = fresh_lane();
+        const int l32e = lane_e & 31, lhie = lane_e >> 5;
+        uint8_t* st = smem + stage_off + wave * 4096;
+        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
+        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
+        const uint32_t wkey = (uint32_t)((l32e >> 1) & 7);
+        // rows past M need no check: the descriptor covers exactly the tile's rows
+        // of D, and offsets past it are dropped
+        const uint32_t rc = (uint32_t)(lane_e & 7);        // read-back: 16-byte chunk of the lane
+        const int rr = lane_e >> 3;                          // read-back: row within 8
+        const uint32_t rd_off = (uint32_t)(rr * 128) + ((rc ^ (uint32_t)((rr >> 1) & 3)) << 4);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {     // 32-column block of the wave tile
+            float snv[4][4];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                if constexpr (!MX) {
+                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + i * 32 + 8 * gq + 4 * lhie);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) snv[gq][t] = t4[t];
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) snv[gq][t] = 1.0f;
+                }
+            }
+            const int n = n0 + wn * WT + 32 * i + 4 * (int)rc;
+            // branch-free select (a compare-and-select here becomes a branch)
+            uint32_t keep = n < N ? 0xFFFFFFFFu : 0u;
+            asm volatile("" : "+v"(keep));
+            const uint32_t col_off = (uint32_t)n * 4u;
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                float smv = 1.0f;
+                if constexpr (!MX) smv = lsa[wm * WT + jb * 32 + l32e];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    v4f w4;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) w4[t] = acc[i][jb][4 * gq + t] * smv * snv[gq][t];
+                    const uint32_t pc = (uint32_t)(2 * gq + lhie) ^ wkey;
+                    *reinterpret_cast<v4f*>(st + l32e * 128 + pc * 16) = w4;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    // band row r = 8k + rr: (r >> 1) & 7 = 4k + (rr >> 1) (mod 8), so the
+                    // physical chunk is rc ^ ((rr >> 1) & 3) ^ 4 (k & 1)
+                    const v4u d = *reinterpret_cast<const v4u*>(st + k * 1024 + (rd_off ^ (uint32_t)(64 * (k & 1))));
+                    const uint32_t mr = (uint32_t)(wm * WT + jb * 32 + 8 * k + rr);   // row inside the tile
+                    const uint32_t off = mr * (uint32_t)N * 4u + col_off;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, ST_NT);
+                }
+                // one block at a time: interleaved across blocks, the schedule kept
+                // too many values live and spilled
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // Staged epilogues: bf16 for N % 8 == 0; fp32 in mode (a) for N % 32 == 0,
+    // rows of whole 128-byte lines (at N = 22012, rows straddling lines, staged
+    // fp32 ran 4% slower than from registers; mode (b) with fp32 output staged
+    // spilled in its main loop)
+    const bool staged = OUT_F32 ? (!MX && (N % 32) == 0) : (N % 8) == 0;
+    auto epilogue_staged_any = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+        if constexpr (OUT_F32) epilogue_staged_f32(j, acc, stage_off);
+        else epilogue_staged(j, acc, stage_off);
+    };
 
     if (nk == 0) {   // K == 0: every tile is the empty sum
         for (int j = 0; j < my_tiles; ++j) {
@@ -589,7 +669,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             tile_scales_to_lds(j, 0);
             wait_vmcnt<0>();
             __syncthreads();
-            if (staged) epilogue_staged(j, acc, 0);
+            if (staged) epilogue_staged_any(j, acc, 0);
             else epilogue(j, acc, 0);
             __syncthreads();
         }
@@ -769,7 +849,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         if (staged) {
             if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
-            epilogue_staged(j, acc, stage_off);
+            epilogue_staged_any(j, acc, stage_off);
             __syncthreads();   // staging reads done before that slot is loaded again
         } else {
             if constexpr (!MX) {

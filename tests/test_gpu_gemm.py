@@ -51,11 +51,14 @@ def uscale(seed, n, stream=3):
 
 # (M, N, K): tile-aligned, ragged in m/n, a K tail that is not a multiple of the
 # 128-byte stage, single elements, several tiles in both directions.  Problems
-# with at most half as many 256x256 tiles as CUs run on 128x128 tiles: the
-# last two shapes have more (2561 x 3000: 11 x 12 tiles of 256) and take the
-# 256x256 kernels, with ragged m, n and a K tail.
+# with at most half as many 256x256 tiles as CUs run on 128x128 tiles; 2561 x
+# 3000 (11 x 12 tiles of 256) and larger take the 256x256 kernels, with ragged
+# m, n and a K tail.  The epilogue depends on N: bf16 is staged through LDS for
+# N % 8 == 0, fp32 for N % 32 == 0 (1000 x 1024, 2600 x 3072, 2561 x 3008);
+# other N store from registers.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
-            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (2561, 3000, 272), (2600, 2900, 1024)]
+            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (2561, 3000, 272),
+            (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
