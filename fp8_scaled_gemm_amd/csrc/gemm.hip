@@ -143,13 +143,14 @@ __host__ __device__ constexpr int share_hi(int k, int n, int s) { return s >= n 
 constexpr int BUF_DW3 = 0x00020000;   // raw (untyped) buffer descriptor word 3, 32-bit data format
 // Cache policy of the staged epilogues' D stores (each store instruction
 // writes 8 rows x 128 contiguous bytes): non-temporal.  Every workgroup writes
-// its finished tile at about the same time (4 MB per XCD for a round of
-// 256x256 bf16 tiles, the size of the XCD's L2); with the default policy that
-// burst displaced the operand panels the XCD's tiles share.  Measured at
-// 8192x22016x8192: 1.4-2% faster in mode (a), 3% in mode (b); at N = 22008
-// (rows not whole lines) still 0.8% (write-through, sc0 sc1: no gain).  The
-// epilogue from registers (16 bytes or less in each of 32 rows per store)
-// keeps the default policy: non-temporal, it ran 30-50% slower.
+// its finished tile at about the same time, 4 MB per XCD for a round of
+// 256x256 bf16 tiles.  Measured at 8192x22016x8192: 1.4-2% faster in mode
+// (a), 3% in mode (b); at N = 22008 (rows not whole lines) still 0.8%
+// (write-through, sc0 sc1: no gain).  The L2 miss traffic of the operand loads
+// is unchanged (FETCH_SIZE), so the gain is in how the writes drain, not in the
+// operands' reuse.  The epilogue from registers (16 bytes or less in each of
+// 32 rows per store) keeps the default policy: non-temporal, it ran 30-50%
+// slower.
 constexpr int ST_NT = 2;
 
 // ---------------------------------------------------------------- helpers
