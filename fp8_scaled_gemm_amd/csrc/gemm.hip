@@ -125,7 +125,7 @@ struct Ring {
     static constexpr int SC_AREA = LDS;
     static constexpr int SC_OPER = TILE * 16;
     static constexpr int SC_BYTES = SCALES ? 4 * SC_OPER : 0;
-    // bf16 epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
+    // epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
     // +16 KB): with 5 slots of 32 KB the slot that is free during the epilogue
     // is borrowed; otherwise (paired, or 16 KB slots) a region of its own
     static constexpr bool OWN_STAGE = PAIRED || TILE != 256;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         asm volatile("" : "+a"(c));
     };
 
-    // ---- epilogue of stream tile j from registers (fp32 output, or N % 8 != 0):
+    // ---- epilogue of stream tile j from registers (where no staged epilogue applies):
     // lane holds m = .. + l32 and n = .. + 8g + 4*lhi + t (t = 0..3) in
     // acc[.][.][4g+t].  Stores over the tile's rows of D: out-of-range lanes get
     // an offset past the end, which the hardware drops.  Mode (a) reads the
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
         }
     };
-    // ---- fp32 epilogue through LDS (mode (a), N % 4 == 0): as the bf16 one, with bands of
+    // ---- fp32 epilogue through LDS (mode (a), N % 32 == 0): as the bf16 one, with bands of
     // one 32x32 block (32 rows x 128 bytes, 4 KB per wave).  Lane (l32, lhi)
     // writes the 16-byte chunks 2 gq + lhi (gq = 0..3) of band row l32, logical
     // chunk c of row r at physical chunk c ^ ((r >> 1) & 7): the writes of 16

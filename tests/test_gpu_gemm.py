@@ -88,14 +88,35 @@ def test_mode_a_raw_cast_workloads(gpu_lib, name):
     assert plain_bad == 0      # N(0,1) operands: the plain fp32-accumulation bound holds everywhere
 
 
-def test_mode_a_k_zero(gpu_lib):
+# k = 0: every output is the empty sum.  The shapes take each epilogue path:
+# from registers (N = 90), staged through LDS on 128-row tiles (300 x 512) and
+# on 256-row tiles (2600 x 3072), for both output types.
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N", [(70, 90), (300, 512), (2600, 3072)])
+def test_mode_a_k_zero(gpu_lib, M, N, out):
     import torch
-    M, N = 70, 90
     A = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
     B = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
     sa, sb = to_dev(uscale(1, M)), to_dev(uscale(2, N))
-    D = torch.full((M, N), 5.0, dtype=torch.float32, device="cuda")
-    gpu_lib.fp8_gemm_scaled(M, N, 0, A, B, sa, sb, D=D, out_dtype=torch.float32)
+    D = torch.full((M, N), 5.0, dtype=torch_dtype(out), device="cuda")
+    say("mode a k=0", M, N, out)
+    gpu_lib.fp8_gemm_scaled(M, N, 0, A, B, sa, sb, D=D, out_dtype=torch_dtype(out))
+    torch.cuda.synchronize()
+    assert bool((D == 0).all())
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N", [(70, 90), (2600, 3072)])
+def test_mode_b_k_zero(gpu_lib, M, N, out):
+    import torch
+    A = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+    B = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    ea = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+    eb = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    D = torch.full((M, N), 5.0, dtype=torch_dtype(out), device="cuda")
+    say("mode b k=0", M, N, out)
+    gpu_lib.mxfp8_gemm(M, N, 0, A, B, ea, eb, D=D, out_dtype=torch_dtype(out))
+    torch.cuda.synchronize()
     assert bool((D == 0).all())
 
 
