@@ -161,7 +161,9 @@ def test_mode_a_one_hot_columns(gpu_lib):
 
 
 def _pipeline(fp8g, w, sample_m, sample_n):
-    """GPU quantize -> GPU GEMM at full size; oracle on the sampled rows/cols."""
+    """GPU quantize -> GPU GEMM at full size, bf16 output (the benchmark's
+    launch) and fp32 output (the staged fp32 epilogue); oracle on the sampled
+    rows/cols."""
     import torch
     say("pipeline", w.name, "draw")
     XA, XB = synth.draw(w, "a"), synth.draw(w, "b")
@@ -170,15 +172,23 @@ def _pipeline(fp8g, w, sample_m, sample_n):
     qb, sb = fp8g.fp8_quantize_rowwise(to_dev(XB))
     D = fp8g.fp8_gemm_scaled(w.M, w.N, w.K, qa, qb, sa, sb)
     torch.cuda.synchronize()
+    Ds = {"bf16": to_host(D)[np.ix_(sample_m, sample_n)]}
+    del D
+    say("pipeline", w.name, "gpu f32")
+    D = fp8g.fp8_gemm_scaled(w.M, w.N, w.K, qa, qb, sa, sb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Ds["f32"] = to_host(D)[np.ix_(sample_m, sample_n)]
+    del D
     oa, osa = oracle_quantize_rows(XA[sample_m])
     ob, osb = oracle_quantize_rows(XB[sample_n])
     # the GPU codes on the sampled rows must be the oracle's, bit for bit
     assert np.array_equal(to_host(qa)[sample_m], oa) and np.array_equal(to_host(sa)[sample_m], osa)
     assert np.array_equal(to_host(qb)[sample_n], ob) and np.array_equal(to_host(sb)[sample_n], osb)
-    Ds = to_host(D)[np.ix_(sample_m, sample_n)]
     ref = gemm.gemm_scaled(oa, ob, osa, osb)
-    return assert_gemm_close(Ds, ref, gemm.gemm_scaled_weight(oa, ob, osa, osb), "bf16", w.name,
-                             gemm.alignment_term(oa, ob, osa, osb))
+    W = gemm.gemm_scaled_weight(oa, ob, osa, osb)
+    T = gemm.alignment_term(oa, ob, osa, osb)
+    for out in ("bf16", "f32"):
+        assert_gemm_close(Ds[out], ref, W, out, "%s %s" % (w.name, out), T)
 
 
 def _samples(total, n, seed):
@@ -280,14 +290,17 @@ def test_mode_b_mx_workload(gpu_lib):
     say("mx workload draw")
     qa, ea = oracle_mx_rows(synth.draw(w, "a"))
     qb, eb = oracle_mx_rows(synth.draw(w, "b"))
-    say("mx workload gpu")
-    D = gpu_lib.mxfp8_gemm(w.M, w.N, w.K, to_dev(qa), to_dev(qb), to_dev(ea), to_dev(eb))
-    torch.cuda.synchronize()
     sm, sn = _samples(w.M, 64, 5), _samples(w.N, 384, 6)
     ref = gemm.mxfp8_gemm(qa[sm], qb[sn], ea[sm], eb[sn])
     W = gemm.mxfp8_gemm_weight(qa[sm], qb[sn], ea[sm], eb[sn])
-    assert_gemm_close(to_host(D)[np.ix_(sm, sn)], ref, W, "bf16", w.name,
-                      gemm.alignment_term(qa[sm], qb[sn], ea=ea[sm], eb=eb[sn]))
+    T = gemm.alignment_term(qa[sm], qb[sn], ea=ea[sm], eb=eb[sn])
+    A, B, EA, EB = to_dev(qa), to_dev(qb), to_dev(ea), to_dev(eb)
+    for out in ("bf16", "f32"):   # the benchmark's launch, and fp32 output from registers
+        say("mx workload gpu", out)
+        D = gpu_lib.mxfp8_gemm(w.M, w.N, w.K, A, B, EA, EB, out_dtype=torch_dtype(out))
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host(D)[np.ix_(sm, sn)], ref, W, out, "%s %s" % (w.name, out), T)
+        del D
 
 
 # Whole scale dwords (K % 128 == 0): the scales of 4 stages at a time are
