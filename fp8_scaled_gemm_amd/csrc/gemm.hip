@@ -105,19 +105,21 @@ struct Geo {
 
 // Ring geometry per kernel variant.  256-row items: 5 slots of 32 KB fill the
 // LDS, so mode (b) with whole scale dwords (scale groups beside the ring)
-// fits only 4 slots.  128-row items: 5 slots of 16 KB.
+// fits only 4 slots.  128-row items: mode (a) 8 slots of 16 KB, loads 7 items
+// ahead (against 5 slots: 7-10% faster at 2048x1024x4096 and the other
+// 128-tile shapes measured); mode (b) 5 (8 slots ran 5% slower there).
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
     using G = Geo<TILE>;
     static constexpr bool SCALES = MX && !KTAIL;
-    static constexpr int NSLOT = (SCALES && TILE == 256) ? 4 : 5;
+    static constexpr int NSLOT = TILE == 256 ? (SCALES ? 4 : 5) : (MX ? 5 : 8);
     static constexpr int SLOT = G::OP_BYTES;
     static constexpr int LDS = NSLOT * SLOT;
     static constexpr int LOADS = G::DMA_PER_ITEM;   // load instructions per item and wave
     // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
     // slots are free (its step 1), so both its items are issued in that step
-    // (none in step 0) to give them the longest lead.  5 slots: one item per
-    // step, four items ahead.
+    // (none in step 0) to give them the longest lead.  5 or more slots: one
+    // item per step, NSLOT-1 items ahead.
     static constexpr bool PAIRED = NSLOT == 4;
     // mode (b) scale groups after the ring: 2 buffers x 2 operands x TILE rows
     // x 16 bytes (the scales of SC_GROUP stages)
@@ -133,7 +135,8 @@ struct Ring {
     static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0);
 };
 static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
-                  Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024, "LDS");
+                  Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024 && Ring<false, false, 128>::LDS_TOTAL <= 160 * 1024,
+              "LDS");
 
 // The share of n items that slot k of s slots takes: one per slot while they
 // last when s >= n, else an even split.
@@ -759,8 +762,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
-            // the next stage's items landed: with 5 slots one later item may be in
-            // flight; with 4 (paired) none
+            // the next stage's items landed: with NSLOT >= 5 slots the NSLOT-4
+            // items issued after them may be in flight; with 4 (paired) none
             wait_vmcnt<(R::PAIRED ? 0 : NSLOT - 4) * LI>();
             __syncthreads();
             // last stage of a tile: the slot of its B item is now free until the
