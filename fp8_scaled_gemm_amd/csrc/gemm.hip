@@ -926,9 +926,14 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     // 128-row tiles when 256-row tiles would leave at least half of the CUs
-    // idle: four times the tiles, each at a lower matrix-core rate
+    // idle: four times the tiles, each at a lower matrix-core rate.  Mode (a)
+    // also when the 256-row tiles spill just past one round (at most an eighth
+    // of a second one): 4352x4096 (272 tiles) ran 4-14% faster on 128-row
+    // tiles at K = 1024..8192, while at 1.5 and 2 rounds the 256-row tiles
+    // were 4-35% faster.
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-    if (2 * tiles256 <= cus) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
+    const bool spill = !MX && tiles256 > cus && 8 * (tiles256 - cus) <= cus;
+    if (2 * tiles256 <= cus || spill) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
     return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
 }
 

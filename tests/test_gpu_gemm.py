@@ -55,12 +55,14 @@ def uscale(seed, n, stream=3):
 # 3000 (11 x 12 tiles of 256) and larger take the 256x256 kernels, with ragged
 # m, n and a K tail.  The epilogue depends on N: bf16 is staged through LDS for
 # N % 8 == 0, fp32 for N % 32 == 0 (1000 x 1024, 2600 x 3072, 2561 x 3008);
-# other N store from registers.  4352 x 4096 and 4352 x 4032 have 272 tiles
+# other N store from registers.  4864 x 4096 and 4864 x 4032 have 304 tiles
 # of 256 for 256 workgroups: a workgroup runs a second tile, so its epilogue
-# borrows a ring slot while the next tile's loads are in flight.
+# borrows a ring slot while the next tile's loads are in flight.  4352 x 4096
+# (272 tiles of 256, just past one round) runs on 1088 tiles of 128.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
             (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (2561, 3000, 272),
-            (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024), (4352, 4096, 256), (4352, 4032, 272)]
+            (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024), (4864, 4096, 256), (4864, 4032, 272),
+            (4352, 4096, 272)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
