@@ -75,7 +75,7 @@ hipError_t launch_quantize_mx(const float* x, int64_t rows, int64_t cols, uint8_
     if (nvec == 0) return hipSuccess;
     const int64_t per_block = (int64_t)MX_THREADS * MX_UNROLL;
     int64_t blocks = (nvec + per_block - 1) / per_block;
-    if (blocks > 4096) blocks = 4096;       // grid-stride beyond: 16 workgroups per CU
+    if (blocks > 8192) blocks = 8192;       // grid-stride beyond: 32 workgroups per CU
     quantize_mx_kernel<<<dim3((unsigned)blocks), dim3(MX_THREADS), 0, stream>>>(
         reinterpret_cast<const v4f*>(x), nvec, reinterpret_cast<uint32_t*>(q), scale);
     return hipGetLastError();
