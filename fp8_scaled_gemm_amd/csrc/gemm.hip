@@ -358,16 +358,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     auto read_scales = [&](int j, int s, int h, uint32_t* xa, uint32_t* xb) __attribute__((always_inline)) {
         if constexpr (MX) {
             if constexpr (R::SCALES) {
-                const uint32_t sh = (uint32_t)(8 * (2 * h + lhi));
+                // the stage's dword holds the scales of its 4 blocks; shifted by
+                // this lane half, byte 2h is step h's block (selected in the
+                // matrix-core instruction), so one read serves both steps.  The
+                // lane-dependent parts come from a fresh lane index: kept live
+                // from the kernel start they were spilled.
+                const int ln = fresh_lane();
+                const int l32s = ln & 31;
+                const uint32_t sh = (uint32_t)(8 * (ln >> 5));
                 const int ub = (j * ngt + s / R::SC_GROUP) & 1;
                 const uint8_t* sca = smem + R::SC_AREA + 2 * ub * R::SC_OPER;
                 const uint8_t* scb = sca + R::SC_OPER;
                 // row wm*WT + 32i + l32: (row >> 3) & 3 == (l32 >> 3) & 3
-                const uint32_t pos = (((uint32_t)(s & 3) + (uint32_t)(l32 >> 3)) & 3u) * 4u;
+                const uint32_t pos = (((uint32_t)(s & 3) + (uint32_t)(l32s >> 3)) & 3u) * 4u;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32) * 16 + pos) >> sh;
-                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32) * 16 + pos) >> sh;
+                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32s) * 16 + pos) >> sh;
+                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32s) * 16 + pos) >> sh;
                 }
             } else {
                 const TileCoord tc = tile_of(j);
@@ -395,9 +402,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // steps past later barriers, leaving the matrix core idle in between.
     // The instruction's first operand is fed from B's rows, so its format
     // field is FB and the second one's FA.
-    auto mfma = [&](v16f& c, const v8i& fbi, const v8i& faj, uint32_t sbi, uint32_t saj) __attribute__((always_inline)) {
+    // OPS: the byte of each scale register that holds this lane's block scale
+    auto mfma = [&](v16f& c, const v8i& fbi, const v8i& faj, uint32_t sbi, uint32_t saj, auto ops_tag)
+                    __attribute__((always_inline)) {
+        constexpr int OPS = decltype(ops_tag)::value;
         if constexpr (MX)
-            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, FB, FA, 0, (int)sbi, 0, (int)saj);
+            c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, FB, FA, OPS, (int)sbi, OPS, (int)saj);
         else
             c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fbi, faj, c, FB, FA, 0, 127, 0, 127);
         asm volatile("" : "+a"(c));
@@ -742,9 +752,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     constexpr int SLOTS = (NB - 1) * NB;
     constexpr int NREAD = 2 * NB;
     constexpr int SCALE_SLOT = R::SCALES ? 0 : (SLOTS > NREAD ? NREAD + 1 : SLOTS - 1);
-    auto kstep = [&](v16f (&acc)[NB][NB], int j, int s, int h, auto last_tag, const v8i* fa, const v8i* fb, v8i* na,
-                     v8i* nbf) __attribute__((always_inline)) {
+    auto kstep = [&](v16f (&acc)[NB][NB], int j, int s, auto h_tag, auto last_tag, const v8i* fa, const v8i* fb,
+                     v8i* na, v8i* nbf) __attribute__((always_inline)) {
+        constexpr int h = decltype(h_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
+        using Ops = std::integral_constant<int, R::SCALES ? 2 * h : 0>;
+        // whole scale dwords are read once per stage, in its step 1 for the next stage
+        constexpr bool READ_SC = !R::SCALES || h == 1;
         bool sc_go = false;
         int sc_gi = 0, sc_ub = 0;
         if constexpr (R::SCALES) {
@@ -759,7 +773,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
         }
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb]);
+        for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb], Ops{});
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
             // the next stage's items landed: with NSLOT >= 5 slots the NSLOT-4
@@ -782,7 +796,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
             const int i = 1 + k / NB, jb = k % NB;
-            mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb]);
+            mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb], Ops{});
             if constexpr (R::SCALES) {
                 if (sc_go) {
                     if constexpr (R::PAIRED) {
@@ -808,7 +822,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
             // reads in order of first use: row block 0 of B, the NB of A, then the rest of B
             if constexpr (!LAST) {
-                if (R::SCALES && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
+                if (R::SCALES && READ_SC && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
 #pragma unroll
                 for (int e = share_lo(k, NREAD, SLOTS); e < share_hi(k, NREAD, SLOTS); ++e) {
                     if (e == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
@@ -824,7 +838,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         // keep this step's operand registers allocated to its end
 #pragma unroll
         for (int i = 0; i < NB; ++i) asm volatile("" : : "v"(fa[i]), "v"(fb[i]));
-        if constexpr (!LAST) {
+        if constexpr (!LAST && READ_SC) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 xa[i] = nxa[i];
@@ -832,6 +846,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
         }
     };
+    using Step0 = std::integral_constant<int, 0>;
+    using Step1 = std::integral_constant<int, 1>;
     using NotLast = std::integral_constant<bool, false>;
     using Last = std::integral_constant<bool, true>;
 
@@ -842,11 +858,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
         for (int s = 0; s < nk - 1; ++s) {
-            kstep(acc, j, s, 0, NotLast{}, fa0, fb0, fa1, fb1);
-            kstep(acc, j, s, 1, NotLast{}, fa1, fb1, fa0, fb0);
+            kstep(acc, j, s, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
+            kstep(acc, j, s, Step1{}, NotLast{}, fa1, fb1, fa0, fb0);
         }
-        kstep(acc, j, nk - 1, 0, NotLast{}, fa0, fb0, fa1, fb1);
-        kstep(acc, j, nk - 1, 1, Last{}, fa1, fb1, fa0, fb0);
+        kstep(acc, j, nk - 1, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
+        kstep(acc, j, nk - 1, Step1{}, Last{}, fa1, fb1, fa0, fb0);
         // the slot of the last stage's B item is free until the next K step
         // loads into it (every wave finished reading it before the last barrier)
         const uint32_t stage_off = R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT);
