@@ -737,9 +737,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   are read after the epilogue, which then has their registers to itself).
     // matrix-core steps after row block 0 (12, or 2 for 128-row tiles); the
     // step's loads and the next step's 2 NB fragment reads are spread over them.
-    // Mode (b) scales from LDS are read first, in slot 0: LDS reads complete in
-    // order, so scales read after the fragments would hold the next step's
-    // first matrix-core instruction until every fragment read had landed.
+    // Mode (b) scales from LDS (once per stage, in its step 1, for the next
+    // stage) are read first, in slot 0: LDS reads complete in order, so scales
+    // read after the fragments would hold the next step's first matrix-core
+    // instruction until every fragment read had landed.
     // Scales loaded byte-wise from global memory (K tail) are read after the
     // step's item loads instead.
     // Mode (b) scale groups: step 0 of a group's first stage loads the next
