@@ -6,7 +6,9 @@ decode from the bit fields, the saturating round-to-nearest-even cast written
 twice -- as the nearest decoded magnitude and as integer bit manipulation --,
 the row-wise quantizer and both GEMM modes in double).  Tests use it to check
 the cast on every fp32 bit pattern and to check the two oracles against each
-other.  build() compiles it with g++ (host only).
+other; its threaded matrix-core truncation term (the definition of
+oracle.gemm.alignment_term) serves the checks of full-size GEMM results.
+build() compiles it with g++ (host only).
 """
 
 import ctypes
@@ -29,7 +31,7 @@ def build() -> str:
     if cxx is None:
         raise RuntimeError("no host C++ compiler (g++) for the C++ oracle")
     tmp = LIB + ".tmp"
-    res = subprocess.run([cxx, "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, SRC], capture_output=True, text=True)
+    res = subprocess.run([cxx, "-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-o", tmp, SRC], capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("building the C++ oracle failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
@@ -51,6 +53,8 @@ def load():
         lib.fp8o_quantize_rowwise.argtypes, lib.fp8o_quantize_rowwise.restype = [I, P, I64, I64, P, P], None
         lib.fp8o_gemm_scaled.argtypes, lib.fp8o_gemm_scaled.restype = [I, I, I64, I64, I64, P, P, P, P, P], None
         lib.fp8o_gemm_mx.argtypes, lib.fp8o_gemm_mx.restype = [I, I, I64, I64, I64, P, P, P, P, P], None
+        lib.fp8o_alignment_term.argtypes = [I, I, I64, I64, I64, P, P, P, P, P, I]
+        lib.fp8o_alignment_term.restype = None
         _lib = lib
     return _lib
 
@@ -105,3 +109,26 @@ def mxfp8_gemm(A, B, ea, eb, fmt_a="e4m3", fmt_b="e4m3"):
     D = np.empty((M, N), np.float64)
     load().fp8o_gemm_mx(FMT[fmt_a], FMT[fmt_b], M, N, K, _p(A), _p(B), _p(ea), _p(eb), _p(D))
     return D
+
+
+def alignment_term(A, B, sa=None, sb=None, ea=None, eb=None, fmt_a="e4m3", fmt_b="e4m3", threads=0):
+    """The matrix-core truncation term T (oracle.gemm.alignment_term's
+    definition), computed by the threaded C++ loop: same arguments."""
+    A, B = np.ascontiguousarray(A, np.uint8), np.ascontiguousarray(B, np.uint8)
+    M, K = A.shape
+    N = B.shape[0]
+    for codes, fmt in ((A, fmt_a), (B, fmt_b)):
+        if not np.isfinite(decode_table(fmt)[codes & 0x7F]).all():
+            raise ValueError("%s NaN or infinity code in a GEMM operand" % fmt)
+    T = np.empty((M, N), np.float64)
+    if ea is not None:
+        ea = np.ascontiguousarray(ea, np.uint8)
+        eb = np.ascontiguousarray(eb, np.uint8)
+        load().fp8o_alignment_term(FMT[fmt_a], FMT[fmt_b], M, N, K, _p(A), _p(B), _p(ea), _p(eb), _p(T), threads)
+    else:
+        load().fp8o_alignment_term(FMT[fmt_a], FMT[fmt_b], M, N, K, _p(A), _p(B), None, None, _p(T), threads)
+    if sa is not None:
+        sa = np.abs(np.asarray(sa, dtype=np.float32).astype(np.float64))
+        sb = np.abs(np.asarray(sb, dtype=np.float32).astype(np.float64))
+        T = T * sa[:, None] * sb[None, :]
+    return T

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from oracle import e4m3, gemm, quant  # noqa: E402
+from oracle import cpp_oracle, e4m3, gemm, quant  # noqa: E402
 
 
 def say(*args):
@@ -50,20 +50,36 @@ def oracle_cast(x, chunk=1 << 18):
     return out.reshape(x.shape)
 
 
-def assert_gemm_close(D_gpu, D_ref, W, out, what="", T=None):
+def alignment(A, B, sa=None, sb=None, ea=None, eb=None, fmt_a="e4m3", fmt_b="e4m3"):
+    """The matrix-core truncation term T of the bound: the numpy definition
+    (oracle.gemm.alignment_term) for small problems, the threaded C++ loop of
+    the same definition (oracle.cpp_oracle.alignment_term) for large ones."""
+    M, K = np.shape(A)
+    N = np.shape(B)[0]
+    if M * N * K <= (1 << 24):
+        return gemm.alignment_term(A, B, sa, sb, ea, eb, fmt_a, fmt_b)
+    return cpp_oracle.alignment_term(A, B, sa, sb, ea, eb, fmt_a, fmt_b)
+
+
+def assert_gemm_close(D_gpu, D_ref, W, out, what="", T=None, plain_max=None):
     """Element-by-element check against the bound 1e-5 W + ulp + T (T: the
-    matrix-core alignment term).  Also reports how many elements meet the
-    plain fp32-accumulation bound (T = 0)."""
+    matrix-core truncation term).  Also counts the elements over the plain
+    fp32-accumulation bound 1e-5 W + ulp (T = 0) and, when plain_max is given,
+    asserts that count is at most plain_max.  Returns (worst error / tolerance
+    with T, elements over the plain bound)."""
     ok, ratio, nbad = gemm.check(D_gpu, D_ref, W, out, T)
-    plain_ok, _, plain_bad = gemm.check(D_gpu, D_ref, W, out)
-    say("%s: worst err/tol %.3g; plain 1e-5 bound met by %d of %d" % (what, ratio, D_ref.size - plain_bad,
-                                                                      D_ref.size))
+    _, plain_ratio, plain_bad = gemm.check(D_gpu, D_ref, W, out)
+    say("%s: worst err/tol %.3g (plain bound: %.3g); plain 1e-5 bound met by %d of %d"
+        % (what, ratio, plain_ratio, D_ref.size - plain_bad, D_ref.size))
     if not ok:
         err = np.abs(np.asarray(D_gpu, np.float64) - D_ref)
         tol = gemm.tolerance(D_ref, W, out, T)
         idx = np.unravel_index(np.argmax(np.where(np.isnan(err), np.inf, err / tol)), err.shape)
         raise AssertionError("%s: %d of %d elements over the bound; worst at %s: gpu %r ref %r tol %r"
                              % (what, nbad, err.size, idx, D_gpu[idx], D_ref[idx], tol[idx]))
+    if plain_max is not None:
+        assert plain_bad <= plain_max, ("%s: %d elements over the plain bound, more than the %d recorded for "
+                                        "these kernels" % (what, plain_bad, plain_max))
     return ratio, plain_bad
 
 

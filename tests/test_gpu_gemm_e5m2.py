@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import assert_gemm_close, say, to_dev, to_host
+from gpu_util import alignment, assert_gemm_close, say, to_dev, to_host
 from oracle import e4m3, e5m2, gemm, quant
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,7 @@ def check_scaled(fp8g, A, fa, B, fb, sa, sb, out, what):
     D = gpu_scaled_ex(fp8g, A, fa, B, fb, sa, sb, out)
     na, nb = NAME[fa], NAME[fb]
     return assert_gemm_close(D, gemm.gemm_scaled(A, B, sa, sb, na, nb), gemm.gemm_scaled_weight(A, B, sa, sb, na, nb),
-                             out, what, gemm.alignment_term(A, B, sa, sb, fmt_a=na, fmt_b=nb))
+                             out, what, alignment(A, B, sa, sb, fmt_a=na, fmt_b=nb))
 
 
 # the last shape has more than half as many 256x256 tiles as CUs: 256x256 kernels
@@ -159,7 +159,7 @@ def test_ex_mode_b_random_codes(gpu_lib, M, N, K, fa, fb, out):
     D = gpu_mx_ex(gpu_lib, A, fa, B, fb, ea, eb, out)
     na, nb = NAME[fa], NAME[fb]
     assert_gemm_close(D, gemm.mxfp8_gemm(A, B, ea, eb, na, nb), gemm.mxfp8_gemm_weight(A, B, ea, eb, na, nb), out,
-                      what, gemm.alignment_term(A, B, ea=ea, eb=eb, fmt_a=na, fmt_b=nb))
+                      what, alignment(A, B, ea=ea, eb=eb, fmt_a=na, fmt_b=nb))
 
 
 def test_ex_mode_b_scale_association_e5m2(gpu_lib):
@@ -201,4 +201,4 @@ def test_ex_mode_b_scale_groups_e5m2(gpu_lib):
     a, b, sa_, sb_ = A[sm], B[sn], ea[sm], eb[sn]
     assert_gemm_close(D[np.ix_(sm, sn)], gemm.mxfp8_gemm(a, b, sa_, sb_, "e5m2", "e5m2"),
                       gemm.mxfp8_gemm_weight(a, b, sa_, sb_, "e5m2", "e5m2"), "bf16", "ex mode b groups e5m2",
-                      gemm.alignment_term(a, b, ea=sa_, eb=sb_, fmt_a="e5m2", fmt_b="e5m2"))
+                      alignment(a, b, ea=sa_, eb=sb_, fmt_a="e5m2", fmt_b="e5m2"))

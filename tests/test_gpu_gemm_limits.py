@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import assert_gemm_close, say, to_dev, to_host
+from gpu_util import alignment, assert_gemm_close, say, to_dev, to_host
 from oracle import gemm
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,7 @@ def test_mode_a_largest_k(gpu_lib, K):
     say("largest k", K)
     D = to_host(gpu_lib.fp8_gemm_scaled(M, N, K, to_dev(A), to_dev(B), to_dev(sa), to_dev(sb), out_dtype=torch_dtype("f32")))
     assert_gemm_close(D, gemm.gemm_scaled(A, B, sa, sb), gemm.gemm_scaled_weight(A, B, sa, sb), "f32",
-                      "largest k %d" % K, gemm.alignment_term(A, B, sa, sb))
+                      "largest k %d" % K, alignment(A, B, sa, sb))
 
 
 def test_mode_b_largest_k(gpu_lib):
@@ -45,7 +45,7 @@ def test_mode_b_largest_k(gpu_lib):
     say("mx largest k", K)
     D = to_host(gpu_lib.mxfp8_gemm(M, N, K, to_dev(A), to_dev(B), to_dev(ea), to_dev(eb), out_dtype=torch_dtype("f32")))
     assert_gemm_close(D, gemm.mxfp8_gemm(A, B, ea, eb), gemm.mxfp8_gemm_weight(A, B, ea, eb), "f32",
-                      "mx largest k", gemm.alignment_term(A, B, ea=ea, eb=eb))
+                      "mx largest k", alignment(A, B, ea=ea, eb=eb))
 
 
 @pytest.mark.parametrize("out,N", [("bf16", 1 << 22), ("f32", 1 << 21)])
@@ -65,7 +65,7 @@ def test_mode_a_largest_n(gpu_lib, out, N):
     D = gpu_lib.fp8_gemm_scaled(M, N, K, to_dev(A), Bd, to_dev(sa), sbd, out_dtype=torch_dtype(out))
     ref = gemm.gemm_scaled(A, base, sa, sb_base)
     W = gemm.gemm_scaled_weight(A, base, sa, sb_base)
-    T = gemm.alignment_term(A, base, sa, sb_base)
+    T = alignment(A, base, sa, sb_base)
     # columns n and n + P*j must hold the same values: compare all N columns
     # against the P reference columns, P-column block by block on the device
     Dh = D.float().cpu().numpy().astype(np.float64) if out == "bf16" else D.cpu().numpy().astype(np.float64)

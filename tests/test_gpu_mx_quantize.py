@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import say, to_dev, to_host
+from gpu_util import alignment, say, to_dev, to_host
 from oracle import quant
 
 pytestmark = pytest.mark.gpu
@@ -98,7 +98,7 @@ def test_mx_quantize_feeds_mxfp8_gemm(gpu_lib):
     oa, oea = quant.mx_quantize(XA)
     ob, oeb = quant.mx_quantize(XB)
     assert_gemm_close(D, gemm.mxfp8_gemm(oa, ob, oea, oeb), gemm.mxfp8_gemm_weight(oa, ob, oea, oeb), "bf16",
-                      "mx quantize -> gemm", gemm.alignment_term(oa, ob, ea=oea, eb=oeb))
+                      "mx quantize -> gemm", alignment(oa, ob, ea=oea, eb=oeb))
 
 
 def test_mx_quantize_deterministic(gpu_lib):

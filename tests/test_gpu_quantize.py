@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import oracle_quantize_rows, say, to_dev, to_host
+from gpu_util import alignment, oracle_quantize_rows, say, to_dev, to_host
 from oracle import quant
 
 pytestmark = pytest.mark.gpu
@@ -364,4 +364,4 @@ def test_quantize_e5m2_feeds_e5m2_gemm(gpu_lib):
     ob, osb = quant.quantize_rowwise(XB)
     assert_gemm_close(D, gemm.gemm_scaled(oa, ob, osa, osb, "e5m2", "e4m3"),
                       gemm.gemm_scaled_weight(oa, ob, osa, osb, "e5m2", "e4m3"), "bf16", "e5m2 quantize -> gemm",
-                      gemm.alignment_term(oa, ob, osa, osb, fmt_a="e5m2", fmt_b="e4m3"))
+                      alignment(oa, ob, osa, osb, fmt_a="e5m2", fmt_b="e4m3"))

@@ -96,3 +96,27 @@ def test_gemms_agree(fa, fb):
     X2 = gemm.mxfp8_gemm(A, B, ea, eb, fa, fb)
     XW = gemm.mxfp8_gemm_weight(A, B, ea, eb, fa, fb)
     assert np.all(np.abs(X1 - X2) <= (2 * K + 4) * 2.0 ** -53 * XW)
+
+
+@pytest.mark.parametrize("fmt_a,fmt_b", [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2")])
+def test_cpp_alignment_term_matches_numpy(fmt_a, fmt_b):
+    """The threaded C++ loop computes the numpy oracle's matrix-core term (mode
+    (a) with scales, mode (b) with block factors, a ragged K)."""
+    def finite(seed, shape, fmt):
+        c = synth.u8_codes(seed, 1, shape, exclude_nan=False)
+        if fmt == "e5m2":
+            return np.where((c & 0x7C) == 0x7C, c & 0xF3, c).astype(np.uint8)
+        return np.where((c & 0x7F) == 0x7F, c & 0xF7, c).astype(np.uint8)
+    A, B = finite(11, (5, 72), fmt_a), finite(12, (7, 72), fmt_b)
+    sa = (0.5 + synth.uniform(synth.stream_key(13, 3), 0, 5)).astype(np.float32)
+    sb = (0.5 + synth.uniform(synth.stream_key(13, 4), 0, 7)).astype(np.float32)
+    for args in ((), (sa, sb)):
+        ref = gemm.alignment_term(A, B, *args, fmt_a=fmt_a, fmt_b=fmt_b)
+        got = cpp_oracle.alignment_term(A, B, *args, fmt_a=fmt_a, fmt_b=fmt_b, threads=3)
+        np.testing.assert_allclose(got, ref, rtol=1e-13, atol=0)
+    A, B = A[:, :64], B[:, :64]
+    ea = (synth.u8_codes(14, 7, (5, 2), exclude_nan=False) % 21 + 117).astype(np.uint8)
+    eb = (synth.u8_codes(14, 8, (7, 2), exclude_nan=False) % 21 + 117).astype(np.uint8)
+    ref = gemm.alignment_term(A, B, ea=ea, eb=eb, fmt_a=fmt_a, fmt_b=fmt_b)
+    got = cpp_oracle.alignment_term(A, B, ea=ea, eb=eb, fmt_a=fmt_a, fmt_b=fmt_b)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=0)

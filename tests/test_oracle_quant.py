@@ -22,6 +22,36 @@ def test_power_of_two_scale_row():
     assert list(q[0]) == [0x7E, 0x30, 0xBC, 0x28, 0x01, 0x08, 0x80, 0x00]
 
 
+def test_quotient_rounds_to_fp32_before_the_cast():
+    """The quotient is the fp32 x / s (reading P2: a correctly rounded fp32
+    divide, then the E4M3 rounding).  These elements make the fp32 quotient
+    land exactly on an E4M3 midpoint while the exact quotient lies just off
+    it, so a float64 divide would round the other way.
+
+    amax = 448 + 7*2^-14 = 448 (1 + 2^-20), so s = amax / 448 = 1 + 2^-20
+    exactly.
+      x1 = 1.0625 + 9*2^-23 = 1.0625 s + 2^-24: x1 / s = 1.0625 + 2^-24 / s,
+        less than half an fp32 ulp (2^-23 near 1) above 1.0625, so
+        fp32(x1 / s) = 1.0625, the midpoint of 1.0 (0x38) and 1.125 (0x39); the
+        tie goes to the even mantissa, 0x38.  Exactly, x1 / s > 1.0625: 0x39.
+      x2 = 1.1875 + 9*2^-23 = 1.1875 s - 2^-24: fp32(x2 / s) = 1.1875, the
+        midpoint of 1.125 (0x39) and 1.25 (0x3A); ties to even: 0x3A.  Exactly,
+        x2 / s < 1.1875: 0x39.
+    The negated elements take the same codes with the sign bit.
+    """
+    amax = 448.0 + 7 * 2.0 ** -14
+    x1 = 1.0625 + 9 * 2.0 ** -23
+    x2 = 1.1875 + 9 * 2.0 ** -23
+    x = np.array([[amax, x1, x2, -x1, -x2]], dtype=np.float32)
+    assert np.array_equal(x.astype(np.float64), np.array([[amax, x1, x2, -x1, -x2]]))   # all exact in fp32
+    q, s = quant.quantize_rowwise(x)
+    assert s[0] == np.float32(1 + 2.0 ** -20)
+    # the two roundings of each quotient, as worked out above
+    assert np.float32(x[0, 1]) / s[0] == np.float32(1.0625) and float(x1) / float(s[0]) > 1.0625
+    assert np.float32(x[0, 2]) / s[0] == np.float32(1.1875) and float(x2) / float(s[0]) < 1.1875
+    assert list(q[0]) == [0x7E, 0x38, 0x3A, 0xB8, 0xBA]
+
+
 def test_unit_scale_row_is_plain_cast():
     # amax 448 -> s = 1: the quantizer reduces to the cast itself.
     rng = np.random.default_rng(7)
