@@ -11,6 +11,11 @@ input already resident in HBM:
       fp8_gemm_scaled(A, B, sa, sb) -> D      (bf16)
       with --fmt-a / --fmt-b e5m2: fp8_quantize_ex(X, fmt) to that operand's
       format and fp8_gemm_scaled_ex (default: both E4M3)
+  c3 (8192 x 2048 x 8192, per-token / per-channel scales): the same three
+      calls as ffn_up
+  c2 (2048 x 1024 x 4096): fp8_gemm_scaled(A, B, sa, sb) -> D (bf16), on
+      N(0,1) operands cast to E4M3 without scaling (cast before the timed
+      region) and U[0.5, 2] scales
   mx (4096 x 14336 x 4096, MXFP8):
       mxfp8_quantize(X_A) -> A, ea            (UE8M0 per 32 K elements)
       mxfp8_quantize(X_B) -> B, eb
@@ -22,6 +27,10 @@ The line also carries
                 per launch / its mean duration from HIP events recorded on the
                 launch stream over the timed region, against the dense FP8 MFMA
                 peak of MI355X (5.0 PFLOP/s);
+                measured_peak: the rate a roof probe reaches in the same run, right
+                after the timed steps (fp8g_roof_mfma: the GEMMs' matrix-core
+                instruction with no memory traffic; fp8g_roof_stream: a stream
+                with the kernel's read/write mix past the infinity cache);
   cpu_baseline: the CPU oracle (numpy, float64) timed on this host on a bounded
                 sample of the same workload, in the same unit.
 """
@@ -42,6 +51,7 @@ import synth  # noqa: E402
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 matrix-core peak
 PEAK_HBM_GBS = 8000.0
 WORKLOADS = {"ffn_up": "c4_ffn_up_8192x22016x8192", "mx": "c5_mx_4096x14336x4096",
+             "c3": "c3_8192x2048x8192", "c2": "c2_2048x1024x4096",
              "concat_mla": "concat_mla_k_fp8_16384x128", "quantize": "c4_ffn_up_8192x22016x8192"}
 CONCAT_T, CONCAT_H = 16384, 128     # tokens x heads, 1-byte elements, rope shared by a token's heads
 
@@ -56,9 +66,9 @@ def log(*a):
 # 40 ms on, for at least a second.  So the warmup covers about 100 ms of work
 # and the timed steps about 60 ms (per mode for the quantize workload).
 CONCAT_SETS = 2    # rotating buffer sets for the concat_mla workload
-QUANT_SETS = 4     # rotating buffer sets for the quantize workload
-DEFAULT_WARMUP = {"ffn_up": 80, "mx": 300, "concat_mla": 1000, "quantize": 1000}
-DEFAULT_STEPS = {"ffn_up": 50, "mx": 200, "concat_mla": 500, "quantize": 500}
+QUANT_SETS = 8     # rotating buffer sets for the quantize workload
+DEFAULT_WARMUP = {"ffn_up": 80, "mx": 300, "c3": 500, "c2": 5000, "concat_mla": 1000, "quantize": 1000}
+DEFAULT_STEPS = {"ffn_up": 50, "mx": 200, "c3": 300, "c2": 3000, "concat_mla": 500, "quantize": 500}
 
 
 def parse():
@@ -69,7 +79,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=None,
                    help="untimed steps first (default: about 100 ms of GPU work for the workload)")
     p.add_argument("--workload", choices=sorted(WORKLOADS), default="ffn_up",
-                   help="ffn_up: the FP8 GEMM path (default); mx: the MXFP8 path; concat_mla: concat_mla_k; "
+                   help="ffn_up: the FP8 GEMM path (default); c3: the same path at 8192x2048x8192; c2: the GEMM "
+                        "at 2048x1024x4096 on raw-cast operands; mx: the MXFP8 path; concat_mla: concat_mla_k; "
                         "quantize: every fp8_quantize_ex mode on the FFN-up activations")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fmt-a", choices=["e4m3", "e5m2"], default="e4m3",
@@ -148,7 +159,6 @@ TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic
                  "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt",
                  "concat_mla": "profiles/concat_mla_k_fp8_16384x128_hbm_traffic.txt",
                  "quantize": "profiles/quantize_rows_f32_e4m3_8192x8192_hbm_traffic.txt"}
-KERNEL_SOURCES = {"ffn_up": "gemm.hip", "mx": "gemm.hip", "concat_mla": "concat.hip", "quantize": "quantize.hip"}
 
 
 def source_digest(name="gemm.hip"):
@@ -188,6 +198,59 @@ def _blas_threads():
     except Exception:
         pass
     return os.cpu_count() or 1
+
+
+def roof_mfma(torch, fp8g, reps=3):
+    """Matrix-core roof at the current clock: the best of `reps` launches of
+    fp8g_roof_mfma (two workgroups per CU, about 2 ms each), in TFLOP/s."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 8000
+    flops = blocks * 4 * iters * 4 * 131072
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fp8g.fp8g_roof_mfma(blocks, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return round(best, 1)
+
+
+def roof_stream(torch, fp8g, write_ratio, nbytes=1 << 30, sets=2, launches=40):
+    """Streaming roof: fp8g_roof_stream over `sets` distinct inputs of nbytes
+    in turn (the measured kernel's own buffer geometry, past the 256 MB
+    infinity cache), `launches` back to back between one event pair (as the
+    streaming kernels themselves are timed), with write-back and with
+    non-temporal stores (which is faster depends on whether the outputs stay
+    in that cache); algorithmic bytes (read + written) per second of the
+    faster policy, in GB/s."""
+    srcs = [torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda") for _ in range(sets)]
+    dsts = [torch.empty(nbytes // write_ratio, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+    moved = nbytes + nbytes // write_ratio
+    best = 0.0
+    for nt in (0, 1):
+        for i in range(2 * sets):
+            fp8g.fp8g_roof_stream(srcs[i % sets], dsts[i % sets], write_ratio, nt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            fp8g.fp8g_roof_stream(srcs[i % sets], dsts[i % sets], write_ratio, nt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, moved * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del srcs, dsts
+    return round(best, 1)
+
+
+def with_measured(roofline, measured, kind):
+    roofline["measured_peak"] = measured
+    roofline["measured_peak_kind"] = kind
+    roofline["frac_of_measured"] = round(roofline["achieved"] / measured, 4) if measured else None
+    return roofline
 
 
 def concat_bench(args, torch, fp8g):
@@ -232,6 +295,9 @@ def concat_bench(args, torch, fp8g):
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                          "traffic": read_traffic(os.path.join(ROOT, TRAFFIC_FILES["concat_mla"]), "concat.hip"),
                          "kernel": "concat_mla_k_kernel", "bytes_per_launch": nbytes}}
+    with_measured(line["roofline"], roof_stream(torch, fp8g, 1),
+                  "fp8g_roof_stream: 1 GiB copy (16 bytes read, 16 written per vector), 2 rotating sets, 40 "
+                  "launches back to back, the faster store policy")
     if not args.no_cpu_baseline:
         from oracle import concat
         ts = 2048                                            # tokens in the sample
@@ -264,9 +330,9 @@ def quantize_bench(args, torch, fp8g):
     dev = torch.device("cuda", 0)
     X = torch.from_numpy(synth.draw(w, "a")).to(dev)
     R, C = X.shape
-    # calls rotate over QUANT_SETS distinct inputs and outputs (1.3 GB for fp32
-    # input), so that the 256 MB infinity cache cannot serve one call's data
-    # to the next
+    # calls rotate over QUANT_SETS distinct inputs and outputs (2.1 GB of fp32
+    # input, 537 MB of codes), so that the 256 MB infinity cache can neither
+    # serve one call's input to the next nor hold the codes written back
     Xs = [X] + [X.clone() for _ in range(QUANT_SETS - 1)]
     Xbs = [x.to(torch.bfloat16) for x in Xs]
     qs = [torch.empty((R, C), dtype=torch.uint8, device=dev) for _ in range(QUANT_SETS)]
@@ -311,6 +377,11 @@ def quantize_bench(args, torch, fp8g):
                          "kernel": "quantize_rows_wg", "bytes_per_launch": head["bytes"]},
             "modes": {k: {"us": v["us"], "gbs": v["gbs"], "frac": round(v["gbs"] / PEAK_HBM_GBS, 4)}
                       for k, v in res.items()}}
+    with_measured(line["roofline"], roof_stream(torch, fp8g, 4, R * C * 4, QUANT_SETS),
+                  "fp8g_roof_stream: %d MiB read, %d MiB written per launch (the fp32 quantizer's 4:1 mix), %d "
+                  "rotating sets, 40 launches back to back, the faster store policy"
+                  % (R * C * 4 >> 20, R * C >> 20, QUANT_SETS))
+    line["copy_roof_gbs"] = roof_stream(torch, fp8g, 1)
     if not args.no_cpu_baseline:
         from oracle import quant
         xs = X[:512].cpu().numpy()
@@ -324,6 +395,69 @@ def quantize_bench(args, torch, fp8g):
                                 "kind": "oracle", "seconds": round(dt * reps, 2),
                                 "sample": "oracle quantize_rowwise (numpy) on the first 512 rows, repeated %d times"
                                           % reps}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_c2(w):
+    """The oracle on the whole 2048x1024x4096 workload: cast both operands
+    (E4M3, no scaling) and form D in float64."""
+    from oracle import e4m3, gemm
+    XA, XB = synth.draw(w, "a"), synth.draw(w, "b")
+    sa, sb = synth.scales(w, "a"), synth.scales(w, "b")
+    t0 = time.perf_counter()
+    qa, qb = e4m3.encode(XA), e4m3.encode(XB)
+    gemm.gemm_scaled(qa, qb, sa, sb)
+    dt = time.perf_counter() - t0
+    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "the whole workload: oracle E4M3 cast of A and B, then all of D in float64 (numpy matmul)"}
+
+
+def gemm_only_bench(args, torch, fp8g, w):
+    """The GEMM alone on raw-cast operands (the DeepGEMM call example's
+    2048x1024x4096): launches back to back between one event pair (a pair
+    per 17 us launch would add its own few us)."""
+    dev = torch.device("cuda", 0)
+    M, N, K = w.M, w.N, w.K
+    A = torch.from_numpy(synth.draw(w, "a")).to(dev).to(torch.float8_e4m3fn)   # N(0,1): no value above 448
+    B = torch.from_numpy(synth.draw(w, "b")).to(dev).to(torch.float8_e4m3fn)
+    sa = torch.from_numpy(synth.scales(w, "a")).to(dev)
+    sb = torch.from_numpy(synth.scales(w, "b")).to(dev)
+    D = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        fp8g.fp8_gemm_scaled(M, N, K, A, B, sa, sb, D=D)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fp8g.fp8_gemm_scaled(M, N, K, A, B, sa, sb, D=D)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    flops = float(w.flops)
+    ms_per_step = elapsed / args.steps * 1e3
+    achieved = flops / (us * 1e-6) / 1e12
+    line = {"metric": "FP8 GEMM TFLOP/s at MxNxK=%dx%dx%d (per-token x per-channel scales, raw-cast operands)"
+                      % (M, N, K),
+            "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+            "data": "synthetic",
+            "config": {"workload": w.name, "M": M, "N": N, "K": K, "out": "bf16",
+                       "mode": "per-token x per-channel scales", "step": "gemm",
+                       "operands": "N(0,1) cast to E4M3 before the timed region; scales U[0.5, 2]"},
+            "kernels_us": {"gemm": round(us, 3)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                         "kernel": "gemm_fp8_kernel", "flops_per_launch": flops}}
+    with_measured(line["roofline"], roof_mfma(torch, fp8g),
+                  "fp8g_roof_mfma: the scaled 32x32x64 FP8 instruction, no memory traffic, best of 3 launches")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline_c2(w)
     print(json.dumps(line), flush=True)
 
 
@@ -353,6 +487,9 @@ def main():
         quantize_bench(args, torch, fp8g)
         return
     w = synth.WORKLOADS[WORKLOADS[args.workload]]
+    if w.prep == "cast":
+        gemm_only_bench(args, torch, fp8g, w)
+        return
     dev = torch.device("cuda", 0)
 
     log("drawing", w.name)
@@ -436,10 +573,13 @@ def main():
     gemm_us = per_kernel["gemm"]
     achieved = flops / (gemm_us * 1e-6) / 1e12
     # the counter summary covers the E4M3 x E4M3 kernel only
-    traffic = read_traffic(args.traffic or os.path.join(ROOT, TRAFFIC_FILES[args.workload])) if e4m3_only else None
+    tf = args.traffic or (os.path.join(ROOT, TRAFFIC_FILES[args.workload]) if args.workload in TRAFFIC_FILES else None)
+    traffic = read_traffic(tf) if e4m3_only else None
+    metric = {"ffn_up": "FP8 GEMM TFLOP/s and % of FP8 MFMA peak at MxNxK=8192x22016x8192",
+              "c3": "FP8 GEMM TFLOP/s at MxNxK=8192x2048x8192 (per-token x per-channel scales)",
+              "mx": "MXFP8 GEMM TFLOP/s at 4096x14336x4096"}[args.workload]
     line = {
-        "metric": "FP8 GEMM TFLOP/s and % of FP8 MFMA peak at MxNxK=8192x22016x8192"
-                  if args.workload == "ffn_up" else "MXFP8 GEMM TFLOP/s at 4096x14336x4096",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -455,7 +595,10 @@ def main():
                    "mode": "per-token x per-channel scales" if w.mode == "a" else "MXFP8",
                    "step": " -> ".join(kernels), "fmt_a": args.fmt_a, "fmt_b": args.fmt_b,
                    "cache": "hot: the GEMM reads the codes the step's quantizers have just written"},
+        "value_basis": "2MNK / mean time of the whole step (%s); the GEMM kernel's own rate is "
+                       "roofline.achieved" % " + ".join(kernels),
         "pct_of_fp8_peak_step": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "gemm_pct_of_fp8_peak": round(100.0 * achieved / PEAK_FP8_TFLOPS, 2),
         "kernels_us": {k: round(v, 2) for k, v in per_kernel.items()},
         "kernels_us_median": {k: round(v, 2) for k, v in per_kernel_median.items()},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
@@ -467,10 +610,15 @@ def main():
     else:   # codes + one scale byte per 32 elements
         qbytes = {"quantize_activations": M * K * 5 + M * K // 32, "quantize_weights": N * K * 5 + N * K // 32}
     line["quantizer_gbs"] = {k: round(b / (per_kernel[k] * 1e-6) / 1e9, 1) for k, b in qbytes.items()}
+    with_measured(line["roofline"], roof_mfma(torch, fp8g),
+                  "fp8g_roof_mfma: the scaled 32x32x64 FP8 instruction, no memory traffic, best of 3 launches")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = (cpu_baseline_ffn_up(w, fa=args.fmt_a, fb=args.fmt_b) if w.mode == "a"
-                                else cpu_baseline_mx(w))
+        if w.mode == "a":
+            m_s, n_s = (4096, 16384) if args.workload == "ffn_up" else (4096, w.N)
+            line["cpu_baseline"] = cpu_baseline_ffn_up(w, m_s, n_s, fa=args.fmt_a, fb=args.fmt_b)
+        else:
+            line["cpu_baseline"] = cpu_baseline_mx(w)
     print(json.dumps(line), flush=True)
 
 

@@ -17,6 +17,8 @@ Functions keep the C names and argument order:
     mxfp8_gemm_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b)       -> D
                                             (fmt: FMT_E4M3 or FMT_E5M2 per operand)
     concat_mla_k(k_nope, k_rope)                         -> k  (MLA key rows)
+    fp8g_roof_mfma(blocks, iters), fp8g_roof_stream(src, dst, write_ratio)
+                                            (roof probes for the benchmark)
 
 E4M3 tensors are ``torch.float8_e4m3fn`` (OCP, the gfx950 format) and E5M2
 tensors ``torch.float8_e5m2``, or either as raw ``torch.uint8`` codes; the
@@ -28,7 +30,8 @@ import os
 import re
 
 __all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
-           "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k", "status_string",
+           "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k", "fp8g_roof_mfma", "fp8g_roof_stream",
+           "status_string",
            "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32", "FMT_E4M3", "FMT_E5M2"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +55,8 @@ _SIGNATURES = {
     "mxfp8_gemm_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
                       ctypes.c_int, _VOIDP],
     "concat_mla_k": [_VOIDP, _VOIDP, _VOIDP, _I64, _I64, _I64, ctypes.c_int, _VOIDP],
+    "fp8g_roof_mfma": [_I64, _I64, _VOIDP, _VOIDP],
+    "fp8g_roof_stream": [_VOIDP, _I64, _VOIDP, ctypes.c_int, ctypes.c_int, _VOIDP],
 }
 
 
@@ -330,3 +335,30 @@ def concat_mla_k(k_nope, k_rope, k=None):
     _check(load().concat_mla_k(_ptr(k), _ptr(k_nope), _ptr(k_rope), T, H, k_rope.shape[1], esz, _stream()),
            "concat_mla_k")
     return k
+
+
+def fp8g_roof_mfma(blocks, iters, sink=None):
+    """Queue the matrix-core roof probe on the current stream: `blocks` x 256
+    threads, each wave `iters` rounds of 4 chains of the scaled 32x32x64
+    instruction (blocks * 4 * iters * 4 * 131072 flops).  Returns the sink
+    tensor (one float, practically never written)."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    _need(sink, "sink", torch.float32)
+    _check(load().fp8g_roof_mfma(int(blocks), int(iters), _ptr(sink), _stream()), "fp8g_roof_mfma")
+    return sink
+
+
+def fp8g_roof_stream(src, dst, write_ratio, nontemporal_stores=0):
+    """Queue the streaming roof probe on the current stream: read all of src
+    (a multiple of 16 bytes), write src.nbytes / write_ratio bytes of dst
+    (write_ratio 1 or 4) with write-back (0) or non-temporal (1) stores."""
+    _need(src, "src")
+    _need(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes // max(int(write_ratio), 1):
+        raise ValueError("dst must hold src.nbytes / write_ratio bytes")
+    _check(load().fp8g_roof_stream(_ptr(src), nbytes, _ptr(dst), int(write_ratio), int(nontemporal_stores),
+                                   _stream()), "fp8g_roof_stream")
+    return dst

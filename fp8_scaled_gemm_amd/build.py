@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp8g.so")
-SOURCES = ["abi.cpp", "quantize.hip", "mx_quantize.hip", "concat.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "quantize.hip", "mx_quantize.hip", "concat.hip", "roof.hip", "gemm.hip"]
 # gemm.hip is compiled once per operand-format pair (FP8G_GEMM_FMT = 2 * fmt_a + fmt_b)
 GEMM_PARTS = 4
 ARCH = "gfx950"

@@ -164,6 +164,23 @@ int concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens
     return hip_status(fp8g::launch_concat_mla_k(k, k_nope, k_rope, tokens, heads, rope_heads, elem_bytes, stream));
 }
 
+int fp8g_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t stream) {
+    if (blocks < 1 || iters < 1 || blocks >= ((int64_t)1 << 31) || iters >= ((int64_t)1 << 31)) return FP8G_ERR_SHAPE;
+    if (!sink) return FP8G_ERR_NULL;
+    return hip_status(fp8g::launch_roof_mfma(blocks, iters, sink, stream));
+}
+
+int fp8g_roof_stream(const void* src, int64_t bytes, void* dst, int write_ratio, int nontemporal_stores,
+                     hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 != 0 || (write_ratio != 1 && write_ratio != 4)) return FP8G_ERR_SHAPE;
+    if (nontemporal_stores != 0 && nontemporal_stores != 1) return FP8G_ERR_DTYPE;
+    if (bytes == 0) return FP8G_OK;
+    if (!src || !dst) return FP8G_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return FP8G_ERR_ALIGN;
+    if (overlaps(range_of(src, bytes), range_of(dst, bytes / write_ratio))) return FP8G_ERR_OVERLAP;
+    return hip_status(fp8g::launch_roof_stream(src, bytes, dst, write_ratio, nontemporal_stores, stream));
+}
+
 const char* fp8g_status_string(int status) {
     switch (status) {
         case FP8G_OK: return "ok";

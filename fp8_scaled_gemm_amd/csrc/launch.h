@@ -32,4 +32,10 @@ hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int
                           int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
                           hipStream_t stream);
 
+// roof probes: matrix-core rate (blocks x 256 threads, iters rounds of 4
+// chains) and streaming bandwidth (bytes read, bytes / write_ratio written)
+hipError_t launch_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t stream);
+hipError_t launch_roof_stream(const void* src, int64_t bytes, void* dst, int write_ratio, int nt,
+                              hipStream_t stream);
+
 }  // namespace fp8g

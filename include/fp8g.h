@@ -302,6 +302,40 @@ int concat_mla_k(void* k, const void* k_nope, const void* k_rope,
                  int64_t tokens, int64_t heads, int64_t rope_heads,
                  int elem_bytes, hipStream_t stream);
 
+/*
+ * fp8g_roof_mfma, fp8g_roof_stream -- roof probes (measurement helpers, not
+ * part of the GEMM path).
+ *
+ * Source: the page on FP8 inference of a 7B model on an RTX 4060, section
+ * 4.1, checks a kernel's core utilisation and memory bandwidth.  These two
+ * calls measure what the chip delivers at the moment they run, so that the
+ * benchmark can put the hot path's kernels beside a measured roof as well as
+ * the nominal one.
+ *
+ * fp8g_roof_mfma: `blocks` workgroups of 256 threads; every wave runs `iters`
+ * rounds of four independent chains of the scaled 32x32x64 FP8 matrix-core
+ * instruction the GEMMs use, with no memory traffic: blocks * 4 * iters * 4 *
+ * 131072 flops.  sink: device, at least one float (practically never written;
+ * it keeps the work).  blocks in [1, 2^31), iters in [1, 2^31), else
+ * ERR_SHAPE; sink NULL: ERR_NULL.
+ *
+ * fp8g_roof_stream: reads `bytes` from src and writes bytes / write_ratio to
+ * dst (write_ratio 1: a copy; 4: 16 bytes read per 4 written, the fp32
+ * quantizer's mix), one 32 KB chunk per workgroup, non-temporal loads, and
+ * write-back (nontemporal_stores 0) or non-temporal (1) stores.  bytes >= 0
+ * and a multiple of 16, write_ratio 1 or 4, else ERR_SHAPE;
+ * nontemporal_stores not 0 or 1: ERR_DTYPE; NULL with bytes > 0: ERR_NULL;
+ * unaligned: ERR_ALIGN; dst overlapping src: ERR_OVERLAP.  dst receives
+ * unspecified bytes.
+ *
+ * Both only queue one kernel on `stream`; the caller times it (HIP events on
+ * the same stream).  Errors: as above, ERR_HIP.
+ */
+int fp8g_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t stream);
+
+int fp8g_roof_stream(const void* src, int64_t bytes, void* dst, int write_ratio, int nontemporal_stores,
+                     hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8g_status_string(int status);
 

@@ -29,7 +29,7 @@ def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
     assert set(names) == {"fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled",
                           "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k",
-                          "fp8g_status_string"}
+                          "fp8g_roof_mfma", "fp8g_roof_stream", "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
 
@@ -224,6 +224,24 @@ def test_concat_mla_k_argument_checks(lib):
     assert cmk(lib, k=P_(4 * 8 * 128)) in (OK, HIP)                  # adjacent
     assert cmk(lib, k=P_((1 << 30) - 16)) == OVERLAP                 # k runs into k_rope
     assert cmk(lib, T=1 << 40, H=1 << 20) == UNSUPPORTED
+
+
+def test_roof_probe_argument_checks(lib):
+    st = ctypes.c_void_p(S)
+    assert lib.fp8g_roof_mfma(0, 10, P_(0), st) == SHAPE
+    assert lib.fp8g_roof_mfma(10, 0, P_(0), st) == SHAPE
+    assert lib.fp8g_roof_mfma(1 << 31, 10, P_(0), st) == SHAPE
+    assert lib.fp8g_roof_mfma(10, 10, None, st) == NULL
+    assert lib.fp8g_roof_stream(P_(0), -16, P_(1 << 30), 1, 0, st) == SHAPE
+    assert lib.fp8g_roof_stream(P_(0), 24, P_(1 << 30), 1, 0, st) == SHAPE      # not a multiple of 16
+    assert lib.fp8g_roof_stream(P_(0), 64, P_(1 << 30), 2, 0, st) == SHAPE      # ratio 1 or 4
+    assert lib.fp8g_roof_stream(None, 0, None, 4, 0, st) == OK                  # empty: no-op
+    assert lib.fp8g_roof_stream(None, 64, P_(1 << 30), 4, 0, st) == NULL
+    assert lib.fp8g_roof_stream(P_(8), 64, P_(1 << 30), 4, 0, st) == ALIGN
+    assert lib.fp8g_roof_stream(P_(0), 64, P_(48), 1, 0, st) == OVERLAP         # dst inside src
+    assert lib.fp8g_roof_stream(P_(0), 64, P_(48), 4, 0, st) == OVERLAP         # 16 bytes written at 48..63
+    assert lib.fp8g_roof_stream(P_(0), 64, P_(64), 1, 0, st) in (OK, HIP)       # adjacent
+    assert lib.fp8g_roof_stream(P_(0), 64, P_(64), 1, 2, st) == DTYPE         # store policy 0 or 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
