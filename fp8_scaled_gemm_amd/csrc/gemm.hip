@@ -73,8 +73,12 @@
 // with a partial EXEC mask yet still writes every lane.  Here they feed only
 // the accumulators and the epilogue, under uniform control flow.
 
+#include <algorithm>
 #include <atomic>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -218,12 +222,18 @@ __device__ __forceinline__ TileCoord tile_coord(int t, int tiles_m, int tiles_n)
 // ---------------------------------------------------------------- kernel
 
 // FA, FB: format code of A and of B (0 = E4M3, 1 = E5M2, as the instruction's
-// format fields)
-template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE>
+// format fields).  SPLIT (mode (a), K a multiple of 128): the tiles past
+// tiles_whole (the last, at most half-full round of tiles) are split over K
+// into `split` equal ranges of stages, one work item each; see the split
+// reduction below.  ws: the items' fp32 partial tiles, cnt: one arrival
+// counter per split tile (zero between launches).
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     int M, int N, int K, const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
     const float* __restrict__ sa, const float* __restrict__ sb, const uint8_t* __restrict__ ea,
-    const uint8_t* __restrict__ eb, void* __restrict__ Dv) {
+    const uint8_t* __restrict__ eb, void* __restrict__ Dv, int tiles_whole, int split, float* __restrict__ ws,
+    int* __restrict__ cnt) {
+    static_assert(!SPLIT || (!MX && !KTAIL), "K splits: mode (a), whole stages");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using GEO = Geo<TILE>;
     constexpr int BM = TILE, BN = TILE, WT = GEO::WT, NB = GEO::NB;
@@ -240,16 +250,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     const int nk = (K + BK - 1) / BK;            // stages per tile
     const int nblk = K / 32;                     // MX scale bytes per row
 
-    // ---- this workgroup's tiles: XCD x = b % 8 owns a contiguous run of tiles;
-    // its W_x workgroups take every W_x-th tile of the run.
+    // ---- this workgroup's work items: XCD x = b % 8 owns a contiguous run of
+    // tiles; its W_x workgroups take every W_x-th tile of the run.  SPLIT: only
+    // the first tiles_whole tiles are walked so; the split items of the
+    // remaining tiles (tile tiles_whole + u, K range s of `split`, item u *
+    // split + s) are distributed over the XCDs the same way, at most one per
+    // workgroup, after its whole tiles.
     const int G = gridDim.x, b = blockIdx.x;
     const int xcd = b % NUM_XCD, slot = b / NUM_XCD;
     const int wx = (G - xcd + NUM_XCD - 1) / NUM_XCD;                 // workgroups on this XCD
-    const int q = total / NUM_XCD, r = total % NUM_XCD;
+    const int n_whole = SPLIT ? tiles_whole : total;
+    const int q = n_whole / NUM_XCD, r = n_whole % NUM_XCD;
     const int run0 = xcd * q + min(xcd, r), runn = q + (xcd < r ? 1 : 0);
-    const int my_tiles = (slot < runn) ? (runn - slot + wx - 1) / wx : 0;
-    const int NS = my_tiles * nk;                                      // stages in this workgroup's stream
-    auto tile_of = [&](int j) __attribute__((always_inline)) { return tile_coord(run0 + slot + j * wx, tiles_m, tiles_n); };
+    const int my_whole = (slot < runn) ? (runn - slot + wx - 1) / wx : 0;
+    int my_split = -1;                                                 // this workgroup's split item, if any
+    if constexpr (SPLIT) {
+        const int ns = (total - tiles_whole) * split;
+        const int q2 = ns / NUM_XCD, r2 = ns % NUM_XCD;
+        if (slot < q2 + (xcd < r2 ? 1 : 0)) my_split = xcd * q2 + min(xcd, r2) + slot;
+    }
+    const int my_tiles = my_whole + (my_split >= 0 ? 1 : 0);          // work items
+    const int nks = SPLIT ? nk / split : nk;                           // stages of a split item
+    const int NS = my_whole * nk + (my_split >= 0 ? nks : 0);          // stages in this workgroup's stream
+    // item j: its tile, first stage (kb) and stages (ns)
+    struct Item {
+        TileCoord tc;
+        int kb, ns;
+    };
+    auto item_of = [&](int j) __attribute__((always_inline)) -> Item {
+        Item it;
+        if (!SPLIT || j < my_whole) {
+            it.tc = tile_coord(run0 + slot + j * wx, tiles_m, tiles_n);
+            it.kb = 0;
+            it.ns = nk;
+        } else {
+            it.tc = tile_coord(tiles_whole + my_split / split, tiles_m, tiles_n);
+            it.kb = (my_split % split) * nks;
+            it.ns = nks;
+        }
+        return it;
+    };
+    auto tile_of = [&](int j) __attribute__((always_inline)) { return item_of(j).tc; };
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;   // LDS byte address of the stage buffers
 
@@ -265,10 +306,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
     const uint32_t dma_voff = (uint32_t)(8 * wave + (lane >> 3)) * (uint32_t)K + dma_chunk * 16u;
     constexpr uint32_t OOB_OFF = 0x80000000u;   // past any panel (panels are < 2^31 bytes)
-    int ij = 0, is = 0, iop = 0, ii = 0, islot = 0;   // cursor: tile, stage in tile, operand, item, its slot
+    int ij = 0, is = 0, iop = 0, ii = 0, islot = 0;   // cursor: work item, stage in it, operand, load item, its slot
+    int ikb = 0, ins = nk;                            // the cursor work item's first stage and stages
     __amdgpu_buffer_rsrc_t rsA, rsB;
     auto cursor_tile = [&]() __attribute__((always_inline)) {
-        const TileCoord tc = tile_of(min(ij, my_tiles - 1));
+        const Item it = item_of(min(ij, my_tiles - 1));
+        const TileCoord tc = it.tc;
+        ikb = it.kb;
+        ins = it.ns;
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows_a = (uint32_t)min(BM, M - m0), rows_b = (uint32_t)min(BN, N - n0);
         rsA = panel(A + (int64_t)m0 * K, rows_a * (uint32_t)K);
@@ -276,9 +321,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     };
     // load q (0..LI-1) of the cursor's item
     auto dma_item = [&](int q) __attribute__((always_inline)) {
-        const int s_ld = (ii < 2 * NS) ? is : nk - 1;   // past the end: reload the last stage
+        const int s_ld = (ii < 2 * NS) ? is : ins - 1;   // past the end: reload the last stage
         const uint32_t sbuf = lds0 + (uint32_t)(islot * SLOT);
-        const uint32_t k0 = (uint32_t)(s_ld * BK);
+        const uint32_t k0 = (uint32_t)((ikb + s_ld) * BK);
         uint32_t voff = dma_voff;
         if constexpr (KTAIL) {
             // bytes past K (the next row's, or past the panel) must read as 0
@@ -324,7 +369,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         islot = (islot + 1 == NSLOT) ? 0 : islot + 1;
         if (++iop == 2) {
             iop = 0;
-            if (++is == nk) {
+            if (++is == ins) {
                 is = 0;
                 ++ij;
                 cursor_tile();
@@ -673,6 +718,88 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         else epilogue_staged(j, acc, stage_off);
     };
 
+    // ---- split reduction (SPLIT: the workgroup's split item, after its last K
+    // step).  Every split item stores its fp32 partial tile to ws (item
+    // u * split + s; per wave and block 4 KB: accumulators 4c .. 4c+3 of lane
+    // L at 1024 c + 16 L, so that every store covers 1 KB in whole lines) and,
+    // once those stores have completed, counts itself
+    // in cnt[u].  The item that arrives last (count split - 1) reads the other
+    // partials and adds all of them in split order, p0 + p1 + ..., its own
+    // from registers, so the sum does not depend on the order of arrival; it
+    // resets cnt[u] to zero for the next launch and returns true: its
+    // workgroup stores the tile.  No workgroup waits for another.
+    // Coherence across the XCDs' separate L2 caches comes from the accesses
+    // themselves, not from fences: the partials are stored and loaded with
+    // device scope (SC1: written through to, and read from, the level all XCDs
+    // share) and the counter is a device-scope atomic.  A device-scope fence
+    // would instead write back and invalidate the whole L2 of the XCD, taking
+    // every other workgroup's operand panels with it (measured: the 2048 x
+    // 1024 x 4096 GEMM ran 3.6x slower so).  The LDS word at stage_off (the
+    // epilogue's staging area, free here) passes the count to all waves.
+    constexpr int CP_SC1 = 16;   // cache policy of the buffer builtins: device scope
+    auto split_reduce = [&](v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) -> bool {
+        const int u = my_split / split, sidx = my_split % split;
+        const int ln = fresh_lane();
+        constexpr uint32_t PART = TILE * TILE * 4;   // bytes per partial tile
+        const __amdgpu_buffer_rsrc_t rw = panel(reinterpret_cast<uint8_t*>(ws) + (size_t)my_split * PART, PART);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const uint32_t off = (uint32_t)((wave * NB * NB + i * NB + jb) * 4096 + ln * 16);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(v4u, (v4f){acc[i][jb][4 * c], acc[i][jb][4 * c + 1], acc[i][jb][4 * c + 2],
+                                                      acc[i][jb][4 * c + 3]}),
+                        rw, off + 1024 * c, 0, CP_SC1);
+            }
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this wave's partial is visible device-wide
+        __syncthreads();
+        int* flag = reinterpret_cast<int*>(smem + stage_off);
+        if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(cnt + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = (old == split - 1) ? 1 : 0;
+        }
+        __syncthreads();
+        const bool last = *flag != 0;
+        __syncthreads();   // every wave has read the flag before that LDS is used again
+        if (!last) return false;
+        const __amdgpu_buffer_rsrc_t rr =
+            panel(reinterpret_cast<uint8_t*>(ws) + (size_t)(u * split) * PART, PART * (uint32_t)split);
+        auto load16 = [&](uint32_t off) __attribute__((always_inline)) -> v16f {
+            const v4f a = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, CP_SC1));
+            const v4f b4 = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 1024, 0, CP_SC1));
+            const v4f c = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 2048, 0, CP_SC1));
+            const v4f d = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rr, off + 3072, 0, CP_SC1));
+            return (v16f){a.x, a.y, a.z, a.w, b4.x, b4.y, b4.z, b4.w, c.x, c.y, c.z, c.w, d.x, d.y, d.z, d.w};
+        };
+        // the split count as a constant, so that every partial's loads of a
+        // block are issued together (a runtime loop waited for each in turn)
+        auto add_parts = [&](auto s_tag) __attribute__((always_inline)) {
+            constexpr int S = decltype(s_tag)::value;
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int jb = 0; jb < NB; ++jb) {
+                    const uint32_t off = (uint32_t)((wave * NB * NB + i * NB + jb) * 4096 + ln * 16);
+                    v16f p[S];
+#pragma unroll
+                    for (int s2 = 0; s2 < S; ++s2)
+                        if (s2 != sidx) p[s2] = load16(s2 * PART + off);
+                    v16f t = sidx == 0 ? acc[i][jb] : p[0];
+#pragma unroll
+                    for (int s2 = 1; s2 < S; ++s2) t += s2 == sidx ? acc[i][jb] : p[s2];
+                    acc[i][jb] = t;
+                }
+        };
+        if (split == 2) add_parts(std::integral_constant<int, 2>{});
+        else if (split == 3) add_parts(std::integral_constant<int, 3>{});
+        else add_parts(std::integral_constant<int, 4>{});
+        if (tid == 0) __hip_atomic_store(cnt + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    };
+
     if (nk == 0) {   // K == 0: every tile is the empty sum
         for (int j = 0; j < my_tiles; ++j) {
             v16f acc[NB][NB];
@@ -858,15 +985,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
-        for (int s = 0; s < nk - 1; ++s) {
+        const int nsj = SPLIT ? item_of(j).ns : nk;   // stages of this work item
+        for (int s = 0; s < nsj - 1; ++s) {
             kstep(acc, j, s, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
             kstep(acc, j, s, Step1{}, NotLast{}, fa1, fb1, fa0, fb0);
         }
-        kstep(acc, j, nk - 1, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
-        kstep(acc, j, nk - 1, Step1{}, Last{}, fa1, fb1, fa0, fb0);
+        kstep(acc, j, nsj - 1, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
+        kstep(acc, j, nsj - 1, Step1{}, Last{}, fa1, fb1, fa0, fb0);
         // the slot of the last stage's B item is free until the next K step
         // loads into it (every wave finished reading it before the last barrier)
         const uint32_t stage_off = R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT);
+        if constexpr (SPLIT) {
+            // the split item is the workgroup's last: the one that does not add
+            // up the tile has no epilogue and nothing after it
+            if (j == my_whole && !split_reduce(acc, stage_off)) break;
+        }
         if (staged) {
             if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
@@ -895,11 +1028,83 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     wait_vmcnt<0>();   // the past-the-end loads must land before the workgroup exits
 }
 
-template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE>
+// ---- split items (mode (a), 128x128 tiles, K a multiple of 128).  When the
+// tiles leave a last round at most half full (r = tiles % CUs tiles, 2r <=
+// CUs), each of those r tiles may be split over K into S equal ranges of
+// stages (S <= min(CUs / r, 4), S dividing the stages, at least 4 stages
+// each), one work item per range, so that the last round keeps up to S r CUs
+// busy instead of r.  Each item's partial tile then goes through memory (see
+// the split reduction in the kernel), so S is chosen by a cost model fitted
+// to measurements on MI355X: a stage of a 128x128 tile takes about 0.37 us
+// whatever the number of tiles (the loop is latency-bound), and the exchange
+// about 1.5 us plus its traffic (every item's 64 KB partial written, S - 1 of
+// S read back) at about 4 TB/s.  Measured against unsplit tiles:
+// 128x128x4096 16.7 -> 12.2 us (S = 4), 2048x1024x8192 31.2 -> 26.3 us
+// (S = 2), 1024x1024x4096 17.1 -> 15.9 us (S = 4); 2048x1024x4096 gained
+// nothing (18.2 / 18.4 us: 16 stages saved, 24 MB exchanged) and
+// 2048x1024x1024 lost 44%, so neither splits.  The workspace holds the arrival
+// counters (one int per split tile, padded to 256 bytes) and the partial
+// tiles (S r <= CUs of them).
+struct SplitPlan {
+    int tiles_whole, split;
+};
+static SplitPlan split_plan(int64_t tiles, int cus, int64_t nk) {
+    constexpr double T_STAGE_US = 0.37, T_FIXED_US = 1.5, BYTES_PER_US = 4.0e6;
+    constexpr double PART_BYTES = 128.0 * 128.0 * 4.0;
+    SplitPlan p{(int)tiles, 1};
+    const int64_t r = tiles % cus;
+    if (r == 0 || 2 * r > cus || nk < 8) return p;
+    double best = 0.1 * (double)nk * T_STAGE_US;   // require a predicted gain of 10% at least
+    for (int s = 2; s <= 4 && s <= cus / r; ++s) {
+        if (nk % s != 0 || nk / s < 4) continue;
+        const double saved = (double)(nk - nk / s) * T_STAGE_US;
+        const double moved = (double)(s * r) * PART_BYTES * (1.0 + (double)(s - 1) / s);
+        const double gain = saved - (T_FIXED_US + moved / BYTES_PER_US);
+        if (gain > best) {
+            best = gain;
+            p.split = s;
+            p.tiles_whole = (int)(tiles - r);
+        }
+    }
+    return p;
+}
+static int64_t ws_cnt_bytes(int cus) { return ((int64_t)cus * 4 + 255) / 256 * 256; }
+// bytes of workspace any split launch on a device with `cus` CUs may use
+static int64_t split_ws_bytes(int cus) { return ws_cnt_bytes(cus) + (int64_t)cus * 256 * 256 * 4; }
+
+// The calling stream's split workspace, allocated (split_ws_bytes) on the
+// stream's first split launch and kept for the life of the process; its
+// counters are cleared on the stream before the first use.  One workspace per
+// (device, stream): launches on one stream run in order, so they never share
+// it at the same time, and other streams have their own.
+static hipError_t stream_workspace(int dev, hipStream_t stream, int cus, void** out) {
+    static std::mutex mu;
+    static std::map<std::pair<int, uintptr_t>, void*> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
+    const auto it = cache.find(key);
+    if (it != cache.end()) {
+        *out = it->second;
+        return hipSuccess;
+    }
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, (size_t)split_ws_bytes(cus));
+    if (e != hipSuccess) return e;
+    e = hipMemsetAsync(p, 0, (size_t)ws_cnt_bytes(cus), stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return e;
+    }
+    cache.emplace(key, p);
+    *out = p;
+    return hipSuccess;
+}
+
+template <bool MX, bool OUT_F32, bool KTAIL, int FA, int FB, int TILE, bool SPLIT>
 static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
                              const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb, void* D,
-                             int dev, int cus, hipStream_t stream) {
-    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB, TILE>;
+                             int dev, int cus, const SplitPlan& sp, void* ws, hipStream_t stream) {
+    auto kern = gemm_fp8_kernel<MX, OUT_F32, KTAIL, FA, FB, TILE, SPLIT>;
     constexpr int LDS_BYTES = Ring<MX, KTAIL, TILE>::LDS_TOTAL;
     // up to 160 KB of dynamic LDS is above the default launch limit; raise it
     // once per device (the attribute is set for the current device).  Setting
@@ -913,29 +1118,52 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
         configured.fetch_or(bit, std::memory_order_release);
     }
     const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
-    const int64_t grid = tiles < cus ? tiles : cus;   // persistent: at most one workgroup per CU
+    const int64_t items = SPLIT ? sp.tiles_whole + (tiles - sp.tiles_whole) * sp.split : tiles;
+    const int64_t grid = items < cus ? items : cus;   // persistent: at most one workgroup per CU
+    int* cnt = SPLIT ? reinterpret_cast<int*>(ws) : nullptr;
+    float* part = SPLIT ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ws_cnt_bytes(cus)) : nullptr;
     kern<<<dim3((unsigned)grid), dim3(NTHREADS), LDS_BYTES, stream>>>((int)m, (int)n, (int)k, A, B, sa, sb, ea,
-                                                                      eb, D);
+                                                                      eb, D, sp.tiles_whole, sp.split, part, cnt);
     return hipGetLastError();
 }
 
 template <bool MX, int FA, int FB, int TILE>
 static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
                                const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, int dev,
-                               int cus, hipStream_t stream) {
+                               int cus, void* fixed_ws, hipStream_t stream) {
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
+    const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
+    if constexpr (!MX && TILE == 128) {   // (256-row tiles: the split kernel would spill around its last step)
+        const SplitPlan sp = split_plan(tiles, cus, k / BK);
+        if (!tail && sp.split > 1) {
+            void* ws = fixed_ws;   // the caller's fixed workspace (of split_ws_bytes(cus) at least), or the stream's
+            if (!ws) {
+                const hipError_t e = stream_workspace(dev, stream, cus, &ws);
+                if (e != hipSuccess) return e;
+            }
+            return out_f32 ? launch_one<MX, true, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D, dev,
+                                                                             cus, sp, ws, stream)
+                           : launch_one<MX, false, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D, dev,
+                                                                              cus, sp, ws, stream);
+        }
+    }
+    const SplitPlan whole{(int)tiles, 1};
     if (out_f32)
-        return tail ? launch_one<MX, true, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream)
-                    : launch_one<MX, true, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream);
-    return tail ? launch_one<MX, false, true, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream)
-                : launch_one<MX, false, false, FA, FB, TILE>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, stream);
+        return tail ? launch_one<MX, true, true, FA, FB, TILE, false>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, whole,
+                                                                      nullptr, stream)
+                    : launch_one<MX, true, false, FA, FB, TILE, false>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus,
+                                                                       whole, nullptr, stream);
+    return tail ? launch_one<MX, false, true, FA, FB, TILE, false>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, whole,
+                                                                   nullptr, stream)
+                : launch_one<MX, false, false, FA, FB, TILE, false>(m, n, k, A, B, sa, sb, ea, eb, D, dev, cus, whole,
+                                                                    nullptr, stream);
 }
 
 template <bool MX, int FA, int FB>
 hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
-                      const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
+                      const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, void* fixed_ws,
                       hipStream_t stream) {
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -950,8 +1178,9 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     // were 4-35% faster.
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
     const bool spill = !MX && tiles256 > cus && 8 * (tiles256 - cus) <= cus;
-    if (2 * tiles256 <= cus || spill) return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
-    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, stream);
+    if (2 * tiles256 <= cus || spill)
+        return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
+    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
 }
 
 // Each operand-format pair's kernels may be compiled in an object of their
@@ -965,10 +1194,10 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
 #define FP8G_FMT_PAIR(KW, FA, FB)                                                                              \
     KW hipError_t launch_fmt<false, FA, FB>(int64_t, int64_t, int64_t, const uint8_t*, const uint8_t*,          \
                                             const float*, const float*, const uint8_t*, const uint8_t*, void*,  \
-                                            int, hipStream_t);                                                  \
+                                            int, void*, hipStream_t);                                           \
     KW hipError_t launch_fmt<true, FA, FB>(int64_t, int64_t, int64_t, const uint8_t*, const uint8_t*,           \
                                            const float*, const float*, const uint8_t*, const uint8_t*, void*,   \
-                                           int, hipStream_t);
+                                           int, void*, hipStream_t);
 
 #if FP8G_GEMM_FMT >= 0
 FP8G_FMT_PAIR(extern template, 0, 0)
@@ -990,13 +1219,13 @@ FP8G_FMT_PAIR(template, 1, 1)
 template <bool MX>
 static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
                               int fmt_b, const float* sa, const float* sb, const uint8_t* ea, const uint8_t* eb,
-                              void* D, int out_f32, hipStream_t stream) {
+                              void* D, int out_f32, void* fixed_ws, hipStream_t stream) {
     if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return hipErrorInvalidValue;
     if (fmt_a == 0)
-        return fmt_b == 0 ? launch_fmt<MX, 0, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream)
-                          : launch_fmt<MX, 0, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream);
-    return fmt_b == 0 ? launch_fmt<MX, 1, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream)
-                      : launch_fmt<MX, 1, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, stream);
+        return fmt_b == 0 ? launch_fmt<MX, 0, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, fixed_ws, stream)
+                          : launch_fmt<MX, 0, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, fixed_ws, stream);
+    return fmt_b == 0 ? launch_fmt<MX, 1, 0>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, fixed_ws, stream)
+                      : launch_fmt<MX, 1, 1>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, fixed_ws, stream);
 }
 
 // 32-bit buffer offsets: a 256-row panel of K bytes stays below 2^31, so the
@@ -1010,14 +1239,14 @@ hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A,
                               int fmt_b, const float* sa, const float* sb, void* D, int out_f32,
                               hipStream_t stream) {
     if (!fits(m, n, k)) return hipErrorInvalidValue;
-    return launch_mode<false>(m, n, k, A, fmt_a, B, fmt_b, sa, sb, nullptr, nullptr, D, out_f32, stream);
+    return launch_mode<false>(m, n, k, A, fmt_a, B, fmt_b, sa, sb, nullptr, nullptr, D, out_f32, nullptr, stream);
 }
 
 hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
                           int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
                           hipStream_t stream) {
     if (!fits(m, n, k)) return hipErrorInvalidValue;
-    return launch_mode<true>(m, n, k, A, fmt_a, B, fmt_b, nullptr, nullptr, ea, eb, D, out_f32, stream);
+    return launch_mode<true>(m, n, k, A, fmt_a, B, fmt_b, nullptr, nullptr, ea, eb, D, out_f32, nullptr, stream);
 }
 #endif  // FP8G_GEMM_FMT <= 0
 

@@ -99,6 +99,42 @@ def test_mode_a_raw_cast_workloads(gpu_lib, name, out):
                       "%s %s" % (name, out), alignment(A, B, sa, sb), plain_max=0)
 
 
+# Shapes whose last round of 128x128 tiles is at most half full, with K long
+# enough for the split to pay, split those tiles over K (S = 2 or 4 items per
+# tile; the last item to finish adds the partials in split order and stores
+# the tile): no whole rounds (128x128x4096: one tile in 4 items; 512x512x8192,
+# 1024x1024x4096, 2048x1024x8192), ragged m and n with the epilogue from
+# registers (1000x1001x8192, N % 8 != 0) or staged (1000x1024x8192), and
+# whole rounds before a split tail (4352x4096x8192: 1024 whole tiles, then 64
+# tiles in 4 items).  Each shape runs three times: the per-tile counters must
+# be back at zero after every launch for the next to add up the same.
+SHAPES_SPLIT = [(128, 128, 4096), (512, 512, 8192), (1000, 1001, 8192), (1000, 1024, 8192), (1024, 1024, 4096),
+                (2048, 1024, 8192), (4352, 4096, 8192)]
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", SHAPES_SPLIT)
+def test_mode_a_split_k(gpu_lib, M, N, K, out):
+    import torch
+    seed = M * 13 + N * 7 + K
+    A, B = codes(seed, (M, K)), codes(seed, (N, K), 2)
+    sa, sb = uscale(seed, M), uscale(seed, N, 4)
+    dA, dB, dsa, dsb = to_dev(A), to_dev(B), to_dev(sa), to_dev(sb)
+    say("mode a split k", M, N, K, out)
+    runs = []
+    for _ in range(3):
+        D = gpu_lib.fp8_gemm_scaled(M, N, K, dA, dB, dsa, dsb, out_dtype=torch_dtype(out))
+        torch.cuda.synchronize()
+        runs.append(D)
+    bits = [r.view(torch.int16 if out == "bf16" else torch.int32) for r in runs]
+    assert torch.equal(bits[0], bits[1]) and torch.equal(bits[0], bits[2]), "split launches differ"
+    Dh = to_host(runs[0])
+    rows = band_rows(M) if M * N > (1 << 20) else np.arange(M)
+    assert_gemm_close(Dh[rows], gemm.gemm_scaled(A[rows], B, sa[rows], sb),
+                      gemm.gemm_scaled_weight(A[rows], B, sa[rows], sb), out,
+                      "split k %dx%dx%d %s" % (M, N, K, out), alignment(A[rows], B, sa[rows], sb))
+
+
 # k = 0: every output is the empty sum.  The shapes take each epilogue path:
 # from registers (N = 90), staged through LDS on 128-row tiles (300 x 512) and
 # on 256-row tiles (2600 x 3072), for both output types.
