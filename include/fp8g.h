@@ -1,7 +1,8 @@
 /*
  * fp8g -- FP8 (OCP E4M3FN) scaled GEMM and row-wise quantizer for AMD Instinct
  * MI355X (gfx950).  Plain C ABI: host-side sizes, device pointers, a HIP
- * stream.  No library state, no allocation, no synchronization.
+ * stream.  No synchronization; the only state and allocation is the split
+ * workspace of fp8_gemm_scaled (see there).
  *
  * Operations (definitions in each entry point's comment):
  *   fp8_quantize_rowwise  fp32 [rows, cols] -> E4M3 codes + one fp32 scale per row
@@ -30,9 +31,12 @@
  *     FP8G_ERR_HIP.  Faults inside a kernel surface at the caller's next
  *     synchronization, as with any HIP kernel.
  *   - Results are bitwise reproducible run to run: sums run in a fixed
- *     order; the one atomic (the per-tensor amax) is a max, which no order
- *     changes.
- *   - Calls are thread-safe: the library keeps no mutable state.
+ *     order; the per-tensor amax atomic is a max, which no order changes,
+ *     and split GEMM tiles add their K ranges' partials in split order
+ *     whichever finishes first.
+ *   - Calls are thread-safe.  The one mutable state is fp8_gemm_scaled's
+ *     split workspace, kept per (device, stream) so that calls on different
+ *     streams never share it.
  */
 #ifndef FP8G_H
 #define FP8G_H
@@ -140,6 +144,14 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
  * scale_a  device, fp32 [m]                   scale_b device, fp32 [n]
  * D        device, [m, n] of out_dtype (fp8g_out_t), written
  * m, n, k >= 0.  m == 0 or n == 0: no-op.  k == 0: D = 0.
+ * Split workspace: when the 128x128 output tiles leave a last round of tiles
+ * at most half full and K (a multiple of 128) is long enough to pay, those
+ * tiles are split over K and their partial sums pass through a device
+ * workspace (with per-tile counters).  The library allocates it with
+ * hipMalloc (64 MB + 1 KB on a 256-CU device) on the first such call on each
+ * (device, stream), clears its counters with hipMemsetAsync on that stream,
+ * and keeps it until the process ends.  That first split call therefore must
+ * not run under stream capture.
  * Limits (ERR_UNSUPPORTED): k % 16 != 0 (16-byte rows); k >= 2^23, m >= 2^31,
  * or n >= 2^22 (bf16 output) / 2^21 (fp32 output): the kernels address a
  * 256-row panel of A, B or D with 32-bit offsets below 2^31.  E4M3 NaN codes
