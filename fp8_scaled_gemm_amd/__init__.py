@@ -12,6 +12,8 @@ Functions keep the C names and argument order:
     fp8_quantize_ex(x, per_tensor=False, fmt=FMT_E4M3)   -> (q, scale)  (fp32 or bf16 x)
     mxfp8_quantize(x)                                    -> (q, scale codes)
     fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b)     -> D
+    fp8_gemm_scaled_noalloc(m, n, k, A, B, scale_a, scale_b, D)  (D given: the
+                                            library allocates nothing)
     mxfp8_gemm(m, n, k, A, B, scale_a, scale_b)          -> D
     fp8_gemm_scaled_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b)  -> D
     mxfp8_gemm_ex(m, n, k, A, fmt_a, B, fmt_b, scale_a, scale_b)       -> D
@@ -29,7 +31,8 @@ import ctypes
 import os
 import re
 
-__all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled", "mxfp8_gemm",
+__all__ = ["load", "fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled",
+           "fp8_gemm_scaled_noalloc", "mxfp8_gemm",
            "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k", "fp8g_roof_mfma", "fp8g_roof_stream",
            "status_string",
            "Fp8gError", "LIB_PATH", "HEADER_PATH", "OUT_BF16", "OUT_F32", "FMT_E4M3", "FMT_E5M2"]
@@ -49,6 +52,7 @@ _SIGNATURES = {
     "mxfp8_quantize": [_VOIDP, _I64, _I64, _VOIDP, _VOIDP, _VOIDP],
     "fp8_quantize_ex": [_VOIDP, ctypes.c_int, _I64, _I64, ctypes.c_int, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP],
     "fp8_gemm_scaled": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
+    "fp8_gemm_scaled_noalloc": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "mxfp8_gemm": [_I64, _I64, _I64, _VOIDP, _VOIDP, _VOIDP, _VOIDP, _VOIDP, ctypes.c_int, _VOIDP],
     "fp8_gemm_scaled_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
                            ctypes.c_int, _VOIDP],
@@ -275,6 +279,23 @@ def fp8_gemm_scaled(m, n, k, A, B, scale_a, scale_b, D=None, out_dtype=None):
     D, code = _out(m, n, A, D, out_dtype)
     _check(load().fp8_gemm_scaled(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D),
                                   code, _stream()), "fp8_gemm_scaled")
+    return D
+
+
+def fp8_gemm_scaled_noalloc(m, n, k, A, B, scale_a, scale_b, D, out_dtype=None):
+    """fp8_gemm_scaled with the library's fixed split workspace: the C call
+    allocates nothing.  D (the output, [m, n] of out_dtype, default bf16) must
+    be given, so that this binding allocates nothing either."""
+    torch = _torch()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if D is None:
+        raise ValueError("fp8_gemm_scaled_noalloc: pass D (the output), the call allocates nothing")
+    Ac, Bc = _gemm_operands(m, n, k, A, B)
+    _need(scale_a, "scale_a", torch.float32, (m,))
+    _need(scale_b, "scale_b", torch.float32, (n,))
+    D, code = _out(m, n, A, D, out_dtype)
+    _check(load().fp8_gemm_scaled_noalloc(m, n, k, _ptr(Ac), _ptr(Bc), _ptr(scale_a), _ptr(scale_b), _ptr(D),
+                                          code, _stream()), "fp8_gemm_scaled_noalloc")
     return D
 
 

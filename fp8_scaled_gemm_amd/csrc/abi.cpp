@@ -132,6 +132,17 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uin
     return fp8_gemm_scaled_ex(m, n, k, A, FP8G_FMT_E4M3, B, FP8G_FMT_E4M3, scale_a, scale_b, D, out_dtype, stream);
 }
 
+int fp8_gemm_scaled_noalloc(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
+                            const float* scale_a, const float* scale_b, void* D, int out_dtype, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 0) return FP8G_ERR_SHAPE;
+    const int st = check_gemm_common(m, n, k, A, B, scale_a, scale_b, m * 4, n * 4, D, out_dtype);
+    if (st >= 0) return st;
+    if (k % 16 != 0) return FP8G_ERR_UNSUPPORTED;
+    const hipError_t e = fp8g::launch_gemm_scaled_noalloc(m, n, k, A, B, scale_a, scale_b, D,
+                                                          out_dtype == FP8G_OUT_F32, stream);
+    return e == hipErrorOutOfMemory ? FP8G_ERR_UNSUPPORTED : hip_status(e);
+}
+
 int mxfp8_gemm_ex(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B, int fmt_b,
                   const uint8_t* scale_a, const uint8_t* scale_b, void* D, int out_dtype, hipStream_t stream) {
     if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return FP8G_ERR_SHAPE;

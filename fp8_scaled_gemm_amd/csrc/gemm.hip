@@ -1242,6 +1242,51 @@ hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A,
     return launch_mode<false>(m, n, k, A, fmt_a, B, fmt_b, sa, sb, nullptr, nullptr, D, out_f32, nullptr, stream);
 }
 
+// ---- fixed split workspace, for callers that cannot allocate
+// (fp8_gemm_scaled_noalloc).  A file-scope device array, SCRATCH_BYTES =
+// split_ws_bytes(256): enough for every split launch on a device of up to 256
+// CUs.  It is zero when the library is loaded (its counters must start at
+// zero) and every split launch leaves its counters at zero again.  In host
+// code the name `scratch` stands for a host-side shadow, not for device
+// memory: its address on each device comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is passed
+// to kernels.  Every call on a device shares that device's array, so calls
+// that overlap on one device race.
+constexpr int64_t SCRATCH_BYTES = (int64_t)256 * 256 * 256 * 4 + 1024;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+static_assert(SCRATCH_BYTES >= (256 * 4 + 255) / 256 * 256 + (int64_t)256 * 256 * 256 * 4, "scratch size");
+
+static hipError_t scratch_address(int dev, void** out) {
+    constexpr int MAX_DEV = 64;
+    static std::mutex mu;
+    static void* addr[MAX_DEV] = {};
+    if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_gemm_scaled_noalloc(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
+                                      const float* sa, const float* sb, void* D, int out_f32, hipStream_t stream) {
+    if (!fits(m, n, k)) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (split_ws_bytes(cus) > SCRATCH_BYTES) return hipErrorOutOfMemory;   // a device of more than 256 CUs
+    void* ws = nullptr;
+    e = scratch_address(dev, &ws);
+    if (e != hipSuccess) return e;
+    return launch_mode<false>(m, n, k, A, 0, B, 0, sa, sb, nullptr, nullptr, D, out_f32, ws, stream);
+}
+
 hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
                           int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
                           hipStream_t stream) {

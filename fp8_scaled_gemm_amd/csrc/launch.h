@@ -27,6 +27,12 @@ hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A,
                               int fmt_b, const float* sa, const float* sb, void* D, int out_f32,
                               hipStream_t stream);
 
+// mode (a), E4M3 operands, with the library's fixed device array as split
+// workspace (no allocation); hipErrorOutOfMemory: the device has more CUs
+// than the array serves
+hipError_t launch_gemm_scaled_noalloc(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B,
+                                      const float* sa, const float* sb, void* D, int out_f32, hipStream_t stream);
+
 // mode (b): UE8M0 scales, one per 32 K elements of every row
 hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,
                           int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,

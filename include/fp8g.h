@@ -11,6 +11,7 @@
  *   mxfp8_quantize        fp32 [rows, cols] -> E4M3 codes + one UE8M0 scale per
  *                         32 consecutive elements of a row (MXFP8)
  *   fp8_gemm_scaled       D[m,n] = sa[m] * sb[n] * sum_k A[m,k] * B[n,k]
+ *   fp8_gemm_scaled_noalloc  the same, allocating nothing (fixed workspace)
  *   mxfp8_gemm            same product with one power-of-two scale per 32 K
  *                         elements of every row of A and of B (MXFP8)
  *   fp8_gemm_scaled_ex,   the two GEMMs with the format of each operand
@@ -151,7 +152,8 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
  * hipMalloc (64 MB + 1 KB on a 256-CU device) on the first such call on each
  * (device, stream), clears its counters with hipMemsetAsync on that stream,
  * and keeps it until the process ends.  That first split call therefore must
- * not run under stream capture.
+ * not run under stream capture; callers that cannot allocate use
+ * fp8_gemm_scaled_noalloc.
  * Limits (ERR_UNSUPPORTED): k % 16 != 0 (16-byte rows); k >= 2^23, m >= 2^31,
  * or n >= 2^22 (bf16 output) / 2^21 (fp32 output): the kernels address a
  * 256-row panel of A, B or D with 32-bit offsets below 2^31.  E4M3 NaN codes
@@ -163,6 +165,28 @@ int fp8_gemm_scaled(int64_t m, int64_t n, int64_t k,
                     const uint8_t* A, const uint8_t* B,
                     const float* scale_a, const float* scale_b,
                     void* D, int out_dtype, hipStream_t stream);
+
+/*
+ * fp8_gemm_scaled_noalloc -- fp8_gemm_scaled for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Same arguments, definition, accuracy, limits and errors as fp8_gemm_scaled,
+ * and the same kernels, so the same D bit for bit.  The one difference is the
+ * split workspace: instead of a per-stream allocation it uses a fixed device
+ * array inside the library (64 MB + 1 KB, zero at load; each device the
+ * library runs on holds its own copy until the process ends).  The call
+ * allocates nothing, clears nothing on the host side, and only queues work on
+ * `stream`; every split launch leaves the array's counters at zero again.
+ * All calls on one device share that array: calls that overlap on one device
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Errors: as fp8_gemm_scaled; ERR_UNSUPPORTED also on a device with more than
+ * 256 CUs, which the array does not cover.
+ */
+int fp8_gemm_scaled_noalloc(int64_t m, int64_t n, int64_t k,
+                            const uint8_t* A, const uint8_t* B,
+                            const float* scale_a, const float* scale_b,
+                            void* D, int out_dtype, hipStream_t stream);
 
 /*
  * fp8_quantize_ex -- FP8 quantization with the scale rule of

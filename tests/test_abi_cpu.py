@@ -28,7 +28,7 @@ def lib():
 def test_exports_every_header_function(lib):
     names = fp8g.header_functions()
     assert set(names) == {"fp8_quantize_rowwise", "fp8_quantize_ex", "mxfp8_quantize", "fp8_gemm_scaled",
-                          "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k",
+                          "fp8_gemm_scaled_noalloc", "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex", "concat_mla_k",
                           "fp8g_roof_mfma", "fp8g_roof_stream", "fp8g_status_string"}
     for name in names:
         assert hasattr(lib, name), name
@@ -47,7 +47,8 @@ def gemm(lib, fn, m, n, k, A=P_(0), B=P_(1 << 30), sa=P_(2 << 30), sb=P_(3 << 30
     return getattr(lib, fn)(m, n, k, A, B, sa, sb, D, out, ctypes.c_void_p(S))
 
 
-@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex"])
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "fp8_gemm_scaled_noalloc", "mxfp8_gemm", "fp8_gemm_scaled_ex",
+                                "mxfp8_gemm_ex"])
 def test_gemm_argument_checks(lib, fn):
     assert gemm(lib, fn, -1, 4, 64) == SHAPE
     assert gemm(lib, fn, 4, -1, 64) == SHAPE
@@ -93,6 +94,7 @@ def test_mx_k_must_be_multiple_of_32(lib):
 def test_scaled_k_must_be_multiple_of_16(lib):
     for k in (8, 24, 33, 1):
         assert gemm(lib, "fp8_gemm_scaled", 4, 4, k) == UNSUPPORTED
+        assert gemm(lib, "fp8_gemm_scaled_noalloc", 4, 4, k) == UNSUPPORTED
         assert gemm(lib, "fp8_gemm_scaled_ex", 4, 4, k) == UNSUPPORTED
 
 
@@ -105,7 +107,8 @@ def test_huge_sizes_rejected(lib):
     assert gemm(lib, "fp8_gemm_scaled", 1 << 40, 1 << 40, 1 << 20) == UNSUPPORTED
 
 
-@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "mxfp8_gemm", "fp8_gemm_scaled_ex", "mxfp8_gemm_ex"])
+@pytest.mark.parametrize("fn", ["fp8_gemm_scaled", "fp8_gemm_scaled_noalloc", "mxfp8_gemm", "fp8_gemm_scaled_ex",
+                                "mxfp8_gemm_ex"])
 def test_gemm_32bit_panel_limits(lib, fn):
     """k < 2^23, m < 2^31, and a 256-row panel of D below 2^31 bytes: n < 2^22
     for bf16 output, n < 2^21 for fp32 output.  Just inside each limit the call
