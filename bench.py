@@ -157,6 +157,8 @@ def cpu_baseline_mx(w, m_s=2048, n_s=8192):
 
 TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic.txt",
                  "mx": "profiles/gemm_mxfp8_mx_4096x14336x4096_hbm_traffic.txt",
+                 "c3": "profiles/gemm_fp8_8192x2048x8192_hbm_traffic.txt",
+                 "c2": "profiles/gemm_fp8_2048x1024x4096_hbm_traffic.txt",
                  "concat_mla": "profiles/concat_mla_k_fp8_16384x128_hbm_traffic.txt",
                  "quantize": "profiles/quantize_rows_f32_e4m3_8192x8192_hbm_traffic.txt"}
 
@@ -451,7 +453,8 @@ def gemm_only_bench(args, torch, fp8g, w):
                        "operands": "N(0,1) cast to E4M3 before the timed region; scales U[0.5, 2]"},
             "kernels_us": {"gemm": round(us, 3)},
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                         "traffic": read_traffic(args.traffic or os.path.join(ROOT, TRAFFIC_FILES["c2"])),
                          "kernel": "gemm_fp8_kernel", "flops_per_launch": flops}}
     with_measured(line["roofline"], roof_mfma(torch, fp8g),
                   "fp8g_roof_mfma: the scaled 32x32x64 FP8 instruction, no memory traffic, best of 3 launches")
