@@ -1072,14 +1072,27 @@ static int64_t ws_cnt_bytes(int cus) { return ((int64_t)cus * 4 + 255) / 256 * 2
 // bytes of workspace any split launch on a device with `cus` CUs may use
 static int64_t split_ws_bytes(int cus) { return ws_cnt_bytes(cus) + (int64_t)cus * 256 * 256 * 4; }
 
-// The calling stream's split workspace, allocated (split_ws_bytes) on the
+// Zeroes n ints (the arrival counters of a new split workspace): a kernel
+// rather than a memset, so that no memset node can reach a captured graph.
+static __global__ __launch_bounds__(256) void clear_counters_kernel(int* __restrict__ p, int n) {
+    const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+    if (i < n) p[i] = 0;
+}
+
+// The calling stream's split workspace (split_ws_bytes), allocated on the
 // stream's first split launch and kept for the life of the process; its
 // counters are cleared on the stream before the first use.  One workspace per
 // (device, stream): launches on one stream run in order, so they never share
-// it at the same time, and other streams have their own.
+// it at the same time, and other streams have their own.  A stream that is
+// being captured into a graph gets its workspace if it has one and nullptr
+// otherwise (nothing is allocated or cleared during a capture): the launch
+// then takes the unsplit schedule.
 static hipError_t stream_workspace(int dev, hipStream_t stream, int cus, void** out) {
     static std::mutex mu;
     static std::map<std::pair<int, uintptr_t>, void*> cache;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(mu);
     const auto key = std::make_pair(dev, reinterpret_cast<uintptr_t>(stream));
     const auto it = cache.find(key);
@@ -1087,10 +1100,14 @@ static hipError_t stream_workspace(int dev, hipStream_t stream, int cus, void** 
         *out = it->second;
         return hipSuccess;
     }
+    *out = nullptr;
+    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, (size_t)split_ws_bytes(cus));
+    e = hipMalloc(&p, (size_t)split_ws_bytes(cus));
     if (e != hipSuccess) return e;
-    e = hipMemsetAsync(p, 0, (size_t)ws_cnt_bytes(cus), stream);
+    const int nc = (int)(ws_cnt_bytes(cus) / 4);
+    clear_counters_kernel<<<dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, stream>>>(reinterpret_cast<int*>(p), nc);
+    e = hipGetLastError();
     if (e != hipSuccess) {
         (void)hipFree(p);
         return e;
@@ -1143,10 +1160,11 @@ static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A
                 const hipError_t e = stream_workspace(dev, stream, cus, &ws);
                 if (e != hipSuccess) return e;
             }
-            return out_f32 ? launch_one<MX, true, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D, dev,
-                                                                             cus, sp, ws, stream)
-                           : launch_one<MX, false, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D, dev,
-                                                                              cus, sp, ws, stream);
+            if (ws)   // none: a capture on a stream without a workspace runs unsplit
+                return out_f32 ? launch_one<MX, true, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D,
+                                                                                 dev, cus, sp, ws, stream)
+                               : launch_one<MX, false, false, FA, FB, TILE, true>(m, n, k, A, B, sa, sb, ea, eb, D,
+                                                                                  dev, cus, sp, ws, stream);
         }
     }
     const SplitPlan whole{(int)tiles, 1};

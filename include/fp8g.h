@@ -150,10 +150,13 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
  * tiles are split over K and their partial sums pass through a device
  * workspace (with per-tile counters).  The library allocates it with
  * hipMalloc (64 MB + 1 KB on a 256-CU device) on the first such call on each
- * (device, stream), clears its counters with hipMemsetAsync on that stream,
- * and keeps it until the process ends.  That first split call therefore must
- * not run under stream capture; callers that cannot allocate use
- * fp8_gemm_scaled_noalloc.
+ * (device, stream), clears its counters with a small kernel on that stream,
+ * and keeps it until the process ends.  Under stream capture nothing is
+ * allocated: a stream that already has its workspace uses it (the graph then
+ * shares it with that stream's later split calls, so the two must not
+ * overlap), and one that has none runs the unsplit schedule, whose D meets
+ * the same bound but may differ in rounding from a split call's.  Callers
+ * that cannot allocate at all use fp8_gemm_scaled_noalloc.
  * Limits (ERR_UNSUPPORTED): k % 16 != 0 (16-byte rows); k >= 2^23, m >= 2^31,
  * or n >= 2^22 (bf16 output) / 2^21 (fp32 output): the kernels address a
  * 256-row panel of A, B or D with 32-bit offsets below 2^31.  E4M3 NaN codes

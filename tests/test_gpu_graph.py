@@ -2,7 +2,9 @@
 GEMM inside one captured graph (torch.cuda.CUDAGraph on the capture stream),
 replay it several times with eager work and synchronizations in between, and
 check every replay against the eager results bit for bit.  The library queues
-kernels only (no memsets, no allocation), so the whole path is capturable."""
+kernels only during a capture (no memsets, no allocation), so the whole path is
+capturable; a mode (a) launch that would take the split-K schedule on a stream
+without its split workspace runs unsplit instead of allocating one."""
 
 import numpy as np
 import pytest
@@ -86,3 +88,79 @@ def test_gemm_deterministic_both_tile_sizes(gpu_lib):
         X2 = gpu_lib.mxfp8_gemm(M, N, K, A, B, ea, eb)
         assert torch.equal(D1.view(torch.int16), D2.view(torch.int16))
         assert torch.equal(X1.view(torch.int16), X2.view(torch.int16))
+
+
+def _split_case():
+    """A mode (a) problem that takes the split-K schedule: one 128x128 tile,
+    K = 4096 (32 stages) split over 4 CUs."""
+    import torch
+    M, N, K = 128, 128, 4096
+    A = synth.u8_codes(57, 1, (M, K))
+    B = synth.u8_codes(57, 2, (N, K))
+    sa = (np.arange(M, dtype=np.float32) % 7 + 1) / 4
+    sb = (np.arange(N, dtype=np.float32) % 5 + 1) / 8
+    t = [torch.from_numpy(x).cuda() for x in (A, B, sa, sb)]
+    return (M, N, K), (A, B, sa, sb), t
+
+
+def test_graph_split_k_on_a_stream_with_workspace(gpu_lib):
+    """Split-K launches captured on a stream that already ran one eagerly (so
+    it has its split workspace): every replay equals the eager result bit for
+    bit, with eager split launches on another stream in between."""
+    import torch
+    (M, N, K), _, (A, B, sa, sb) = _split_case()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        D = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb)
+        F = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eager = (D.clone(), F.clone())
+    g = torch.cuda.CUDAGraph()
+    say("graph split-K: capture on a stream with a workspace")
+    with torch.cuda.graph(g, stream=s):
+        gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb, D=D)
+        gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb, D=F, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        D.fill_(7.0)
+        F.zero_()
+        X = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb)      # eager split launch, current stream
+        torch.cuda.synchronize()
+        assert torch.equal(X.view(torch.int16), eager[0].view(torch.int16))
+        say("graph split-K: replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(D.view(torch.int16), eager[0].view(torch.int16)), rep
+        assert torch.equal(F.view(torch.int32), eager[1].view(torch.int32)), rep
+
+
+def test_graph_split_k_on_a_fresh_stream(gpu_lib):
+    """A split-K-sized problem captured on a stream that has no split
+    workspace yet: nothing is allocated during the capture, the launch takes
+    the unsplit schedule, and every replay meets the accuracy bound against
+    the oracle."""
+    import torch
+    from gpu_util import alignment, assert_gemm_close
+    from oracle import gemm
+    (M, N, K), (A_h, B_h, sa_h, sb_h), (A, B, sa, sb) = _split_case()
+    F = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    say("graph split-K: capture on a fresh stream")
+    with torch.cuda.graph(g, stream=s):
+        gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb, D=F, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = gemm.gemm_scaled(A_h, B_h, sa_h, sb_h)
+    W = gemm.gemm_scaled_weight(A_h, B_h, sa_h, sb_h)
+    T = alignment(A_h, B_h, sa_h, sb_h)
+    first = None
+    for rep in range(3):
+        F.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = F.cpu().numpy()
+        assert_gemm_close(got, ref, W, "f32", "graph split-K fresh stream, replay %d" % rep, T=T)
+        if first is None:
+            first = got.copy()
+        assert np.array_equal(got.view(np.int32), first.view(np.int32))
