@@ -96,15 +96,20 @@ constexpr int NTHREADS = 256;
 constexpr int NUM_XCD = 8;
 constexpr int GROUP_M = 8;
 
-// Tile geometry: a TILE x TILE output tile per workgroup (TILE = 256, or 128
-// for problems with few tiles), 4 waves in 2x2, each wave WT x WT = NB x NB
-// blocks of 32x32.
+// Tile geometry: a BM x BN output tile per workgroup (BM rows of A, BN rows of
+// B), 4 waves in 2x2, each wave WTM x WTN = NBM x NBN blocks of 32x32.  TILE
+// names the shape: 256 (256x256), 128 (128x128, for problems with few
+// tiles) or 64 (64x128, mode (a), for problems whose 128x128 tiles would
+// leave at least half of the CUs idle).
 template <int TILE>
 struct Geo {
-    static constexpr int WT = TILE / 2;                        // wave tile edge
-    static constexpr int NB = WT / 32;                         // blocks per wave-tile edge: 4 or 2
-    static constexpr int OP_BYTES = TILE * BK;                 // one operand of one stage (an "item"): 32 or 16 KB
-    static constexpr int DMA_PER_ITEM = OP_BYTES / 1024 / 4;   // 1 KB per wave instruction, 4 waves: 8 or 4
+    static constexpr int BM = TILE, BN = TILE == 64 ? 128 : TILE;
+    static constexpr int WTM = BM / 2, WTN = BN / 2;           // wave tile
+    static constexpr int NBM = WTM / 32, NBN = WTN / 32;       // blocks per wave tile: 4x4, 2x2 or 1x2
+    // one operand of one stage (an "item"), and its loads per wave (1 KB per
+    // wave instruction, 4 waves)
+    static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+    static constexpr int LA = A_BYTES / 1024 / 4, LB = B_BYTES / 1024 / 4;
 };
 
 // Ring geometry per kernel variant.  256-row items: 5 slots of 32 KB fill the
@@ -115,11 +120,12 @@ struct Geo {
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
     using G = Geo<TILE>;
+    static_assert(!MX || G::BM == G::BN, "mode (b): square tiles");
     static constexpr bool SCALES = MX && !KTAIL;
     static constexpr int NSLOT = TILE == 256 ? (SCALES ? 4 : 5) : (MX ? 5 : 8);
-    static constexpr int SLOT = G::OP_BYTES;
+    static constexpr int SLOT = G::B_BYTES > G::A_BYTES ? G::B_BYTES : G::A_BYTES;
     static constexpr int LDS = NSLOT * SLOT;
-    static constexpr int LOADS = G::DMA_PER_ITEM;   // load instructions per item and wave
+    static constexpr int LA = G::LA, LB = G::LB;   // load instructions per item and wave, A and B
     // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
     // slots are free (its step 1), so both its items are issued in that step
     // (none in step 0) to give them the longest lead.  5 or more slots: one
@@ -129,7 +135,7 @@ struct Ring {
     // x 16 bytes (the scales of SC_GROUP stages)
     static constexpr int SC_GROUP = 4;
     static constexpr int SC_AREA = LDS;
-    static constexpr int SC_OPER = TILE * 16;
+    static constexpr int SC_OPER = G::BM * 16;
     static constexpr int SC_BYTES = SCALES ? 4 * SC_OPER : 0;
     // epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
     // +16 KB): with 5 slots of 32 KB the slot that is free during the epilogue
@@ -139,7 +145,8 @@ struct Ring {
     static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0);
 };
 static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
-                  Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024 && Ring<false, false, 128>::LDS_TOTAL <= 160 * 1024,
+                  Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024 && Ring<false, false, 128>::LDS_TOTAL <= 160 * 1024 &&
+                  Ring<false, false, 64>::LDS_TOTAL <= 160 * 1024,
               "LDS");
 
 // The share of n items that slot k of s slots takes: one per slot while they
@@ -233,11 +240,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     const float* __restrict__ sa, const float* __restrict__ sb, const uint8_t* __restrict__ ea,
     const uint8_t* __restrict__ eb, void* __restrict__ Dv, int tiles_whole, int split, float* __restrict__ ws,
     int* __restrict__ cnt) {
-    static_assert(!SPLIT || (!MX && !KTAIL), "K splits: mode (a), whole stages");
+    static_assert(!SPLIT || (!MX && !KTAIL && TILE == 128), "K splits: mode (a), whole stages, 128x128 tiles");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using GEO = Geo<TILE>;
-    constexpr int BM = TILE, BN = TILE, WT = GEO::WT, NB = GEO::NB;
-    constexpr int OP_BYTES = GEO::OP_BYTES, DMA_PER_ITEM = GEO::DMA_PER_ITEM;
+    constexpr int BM = GEO::BM, BN = GEO::BN, WTM = GEO::WTM, WTN = GEO::WTN, NBM = GEO::NBM, NBN = GEO::NBN;
+    constexpr int NBX = NBM > NBN ? NBM : NBN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -300,7 +307,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // stream the last stage is loaded again (never read), so every K step
     // issues the same number of loads.
     using R = Ring<MX, KTAIL, TILE>;
-    constexpr int NSLOT = R::NSLOT, SLOT = R::SLOT, LI = R::LOADS;
+    constexpr int NSLOT = R::NSLOT, SLOT = R::SLOT, LA = R::LA, LB = R::LB;
+    static_assert(!R::PAIRED || LA == LB, "paired ring: square tiles");
+    // loads of n consecutive items that start with an A item
+    auto loads_of = [](int n) constexpr { return (n + 1) / 2 * LA + n / 2 * LB; };
     // lane L of wave w, instruction p fills row 32p + 8w + L/8, slot L%8, which
     // holds logical chunk (L%8) ^ ((row >> 1) & 7) = (L%8) ^ ((4w + L/16) & 7)
     const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         rsA = panel(A + (int64_t)m0 * K, rows_a * (uint32_t)K);
         rsB = panel(B + (int64_t)n0 * K, rows_b * (uint32_t)K);
     };
-    // load q (0..LI-1) of the cursor's item
+    // load q (0..LA-1 or 0..LB-1) of the cursor's item
     auto dma_item = [&](int q) __attribute__((always_inline)) {
         const int s_ld = (ii < 2 * NS) ? is : ins - 1;   // past the end: reload the last stage
         const uint32_t sbuf = lds0 + (uint32_t)(islot * SLOT);
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // row 16p + L/4 at position L % 4: 16 bytes of a row in one or two lines,
     // where loading each stage's dword alone touches a line per row per stage.
     // Wave w issues loads p = w, w+4, ... of both operands.
-    constexpr int SC_LOADS = R::SCALES ? 2 * (TILE / 16) / 4 : 0;   // per wave and group: 8 or 4
+    constexpr int SC_LOADS = R::SCALES ? 2 * (BM / 16) / 4 : 0;   // per wave and group: 8 or 4
     const int ngt = (nk + R::SC_GROUP - 1) / R::SC_GROUP;            // groups per tile
     const uint32_t sc_voff = (uint32_t)(16 * wave + (lane >> 2)) * (uint32_t)nblk +
                              4u * (((uint32_t)(lane & 3) - (uint32_t)(2 * wave + (lane >> 5))) & 3u);
@@ -380,8 +390,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // ---- fragment reads: step h of the stage whose items sit in LDS slots
     // sa_off (A) and sb_off (B); this lane's rows, chunks 4h + lhi and 4h + 2 + lhi
     const uint32_t key = (uint32_t)((l32 >> 1) & 7);
-    const uint32_t frag_a = (uint32_t)((wm * WT + l32) * BK);
-    const uint32_t frag_b = (uint32_t)((wn * WT + l32) * BK);
+    const uint32_t frag_a = (uint32_t)((wm * WTM + l32) * BK);
+    const uint32_t frag_b = (uint32_t)((wn * WTN + l32) * BK);
     const uint32_t c0 = ((uint32_t)lhi ^ key) << 4, c1 = ((uint32_t)(2 + lhi) ^ key) << 4;
     auto frag = [&](uint32_t slot_off, uint32_t row_off, int h, int i) __attribute__((always_inline)) -> v8i {
         const uint8_t* p = smem + slot_off + row_off + i * 32 * BK;
@@ -414,12 +424,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                 const int ub = (j * ngt + s / R::SC_GROUP) & 1;
                 const uint8_t* sca = smem + R::SC_AREA + 2 * ub * R::SC_OPER;
                 const uint8_t* scb = sca + R::SC_OPER;
-                // row wm*WT + 32i + l32: (row >> 3) & 3 == (l32 >> 3) & 3
+                // row wm*WTM + 32i + l32: (row >> 3) & 3 == (l32 >> 3) & 3
                 const uint32_t pos = (((uint32_t)(s & 3) + (uint32_t)(l32s >> 3)) & 3u) * 4u;
 #pragma unroll
-                for (int i = 0; i < NB; ++i) {
-                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WT + i * 32 + l32s) * 16 + pos) >> sh;
-                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WT + i * 32 + l32s) * 16 + pos) >> sh;
+                for (int i = 0; i < NBM; ++i) {
+                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WTM + i * 32 + l32s) * 16 + pos) >> sh;
+                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WTN + i * 32 + l32s) * 16 + pos) >> sh;
                 }
             } else {
                 const TileCoord tc = tile_of(j);
@@ -430,11 +440,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                 const bool in = kb < nblk;
                 const uint32_t kc = (uint32_t)min(kb, nblk - 1);
 #pragma unroll
-                for (int i = 0; i < NB; ++i) {
+                for (int i = 0; i < NBM; ++i) {
                     const uint32_t va = __builtin_amdgcn_raw_buffer_load_b8(
-                        pa, (uint32_t)(wm * WT + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
+                        pa, (uint32_t)(wm * WTM + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
                     const uint32_t vb = __builtin_amdgcn_raw_buffer_load_b8(
-                        pb, (uint32_t)(wn * WT + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
+                        pb, (uint32_t)(wn * WTN + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
                     xa[i] = in ? va : 127u;
                     xb[i] = in ? vb : 127u;
                 }
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // also wait for the next tile's operand loads in flight.
     constexpr int ESZ = OUT_F32 ? 4 : 2;
     constexpr uint32_t SC_OFF = 16384;   // the tile's sa at stage_off + 16 KB, sb at + 17 KB
-    auto epilogue = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+    auto epilogue = [&](int j, v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) {
         const TileCoord tc = tile_of(j);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows = (uint32_t)min(BM, M - m0);
@@ -479,20 +489,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int l32 = lane_u & 31, lhi = lane_u >> 5;
         const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
         const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
-        float smv[NB], snv[NB][4][4];
+        float smv[NBM], snv[NBN][4][4];
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
+        for (int jb = 0; jb < NBM; ++jb) {
             smv[jb] = 1.0f;
-            if constexpr (!MX) smv[jb] = lsa[wm * WT + jb * 32 + l32];   // rows past M hold 0 (and are not stored)
+            if constexpr (!MX) smv[jb] = lsa[wm * WTM + jb * 32 + l32];   // rows past M hold 0 (and are not stored)
         }
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NBN; ++i)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 if constexpr (!MX) {
                     // a float vector: __builtin_bit_cast of an element of an integer
                     // vector reads element 0 whatever the index (clang)
-                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + i * 32 + 8 * gq + 4 * lhi);
+                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WTN + i * 32 + 8 * gq + 4 * lhi);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) snv[i][gq][t] = t4[t];
                 } else {
@@ -503,15 +513,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const bool vec_ok = (N % 4) == 0;
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            const int mr = wm * WT + jb * 32 + l32;          // row inside the tile
+        for (int jb = 0; jb < NBM; ++jb) {
+            const int mr = wm * WTM + jb * 32 + l32;          // row inside the tile
             const bool mok = m0 + mr < M;
             const uint32_t rowoff = (uint32_t)mr * (uint32_t)N;
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
+            for (int i = 0; i < NBN; ++i) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int n = n0 + wn * WT + i * 32 + 8 * gq + 4 * lhi;
+                    const int n = n0 + wn * WTN + i * 32 + 8 * gq + 4 * lhi;
                     float v[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
@@ -567,7 +577,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                  panel(sb + n0, (uint32_t)min(BN, N - n0) * 4u), 0u);
         }
     };
-    auto epilogue_staged = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+    auto epilogue_staged = [&](int j, v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) {
         const TileCoord tc = tile_of(j);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows = (uint32_t)min(BM, M - m0);
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int rr = lane_e >> 3;                          // read-back: row within 8
         const uint32_t rd_off = (uint32_t)(rr * 128) + ((rc ^ (uint32_t)((rr >> 1) & 3)) << 4);
 #pragma unroll
-        for (int ih = 0; ih < NB / 2; ++ih) {     // 64-column part of the wave tile: blocks i = 2ih, 2ih+1
+        for (int ih = 0; ih < NBN / 2; ++ih) {     // 64-column part of the wave tile: blocks i = 2ih, 2ih+1
             float snv[2][4][4];
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
@@ -595,7 +605,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     if constexpr (!MX) {
                         // a float vector: __builtin_bit_cast of an element of an integer
                         // vector reads element 0 whatever the index (clang)
-                        const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + (2 * ih + ii) * 32 + 8 * gq + 4 * lhie);
+                        const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WTN + (2 * ih + ii) * 32 + 8 * gq + 4 * lhie);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) snv[ii][gq][t] = t4[t];
                     } else {
@@ -604,9 +614,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     }
                 }
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
+            for (int jb = 0; jb < NBM; ++jb) {
                 float smv = 1.0f;
-                if constexpr (!MX) smv = lsa[wm * WT + jb * 32 + l32e];
+                if constexpr (!MX) smv = lsa[wm * WTM + jb * 32 + l32e];
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -619,7 +629,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                         const uint32_t pc = (uint32_t)(4 * ii + gq) ^ wkey;
                         *reinterpret_cast<v2u*>(st + l32e * 128 + pc * 16 + whalf * 8) = w2;
                     }
-                const int n = n0 + wn * WT + 64 * ih + 8 * (int)rc;
+                const int n = n0 + wn * WTN + 64 * ih + 8 * (int)rc;
                 // branch-free select (a compare-and-select here becomes a branch)
                 uint32_t keep = n < N ? 0xFFFFFFFFu : 0u;
                 asm volatile("" : "+v"(keep));
@@ -630,7 +640,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     // physical chunk is rc ^ ((rr >> 1) & 3) ^ 4 (k & 1)
                     v4u d = *reinterpret_cast<const v4u*>(st + k * 1024 + (rd_off ^ (uint32_t)(64 * (k & 1))));
                     if (k >= 2) d = (v4u){d.z, d.w, d.x, d.y};   // rows 16..31: halves swapped
-                    const uint32_t mr = (uint32_t)(wm * WT + jb * 32 + 8 * k + rr);   // row inside the tile
+                    const uint32_t mr = (uint32_t)(wm * WTM + jb * 32 + 8 * k + rr);   // row inside the tile
                     const uint32_t off = mr * (uint32_t)N * 2u + col_off;
                     __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, ST_NT);
                 }
@@ -644,7 +654,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // lanes (16 rows, one chunk) and the reads of 16 lanes (2 rows, 8 chunks)
     // both hit 16 distinct 16-byte bank groups.  Read back row-contiguously, 8
     // lanes store one 128-byte row of the band, as whole lines.
-    auto epilogue_staged_f32 = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+    auto epilogue_staged_f32 = [&](int j, v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) {
         const TileCoord tc = tile_of(j);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
         const uint32_t rows = (uint32_t)min(BM, M - m0);
@@ -663,12 +673,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int rr = lane_e >> 3;                          // read-back: row within 8
         const uint32_t rd_off = (uint32_t)(rr * 128) + ((rc ^ (uint32_t)((rr >> 1) & 3)) << 4);
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {     // 32-column block of the wave tile
+        for (int i = 0; i < NBN; ++i) {     // 32-column block of the wave tile
             float snv[4][4];
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 if constexpr (!MX) {
-                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WT + i * 32 + 8 * gq + 4 * lhie);
+                    const v4f t4 = *reinterpret_cast<const v4f*>(lsb + wn * WTN + i * 32 + 8 * gq + 4 * lhie);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) snv[gq][t] = t4[t];
                 } else {
@@ -676,15 +686,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     for (int t = 0; t < 4; ++t) snv[gq][t] = 1.0f;
                 }
             }
-            const int n = n0 + wn * WT + 32 * i + 4 * (int)rc;
+            const int n = n0 + wn * WTN + 32 * i + 4 * (int)rc;
             // branch-free select (a compare-and-select here becomes a branch)
             uint32_t keep = n < N ? 0xFFFFFFFFu : 0u;
             asm volatile("" : "+v"(keep));
             const uint32_t col_off = (uint32_t)n * 4u;
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
+            for (int jb = 0; jb < NBM; ++jb) {
                 float smv = 1.0f;
-                if constexpr (!MX) smv = lsa[wm * WT + jb * 32 + l32e];
+                if constexpr (!MX) smv = lsa[wm * WTM + jb * 32 + l32e];
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     v4f w4;
@@ -698,7 +708,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                     // band row r = 8k + rr: (r >> 1) & 7 = 4k + (rr >> 1) (mod 8), so the
                     // physical chunk is rc ^ ((rr >> 1) & 3) ^ 4 (k & 1)
                     const v4u d = *reinterpret_cast<const v4u*>(st + k * 1024 + (rd_off ^ (uint32_t)(64 * (k & 1))));
-                    const uint32_t mr = (uint32_t)(wm * WT + jb * 32 + 8 * k + rr);   // row inside the tile
+                    const uint32_t mr = (uint32_t)(wm * WTM + jb * 32 + 8 * k + rr);   // row inside the tile
                     const uint32_t off = mr * (uint32_t)N * 4u + col_off;
                     __builtin_amdgcn_raw_buffer_store_b128(d, rsD, (off & keep) | (OOB & ~keep), 0, ST_NT);
                 }
@@ -713,7 +723,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // fp32 ran 4% slower than from registers; mode (b) with fp32 output staged
     // spilled in its main loop)
     const bool staged = OUT_F32 ? (!MX && (N % 32) == 0) : (N % 8) == 0;
-    auto epilogue_staged_any = [&](int j, v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) {
+    auto epilogue_staged_any = [&](int j, v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) {
         if constexpr (OUT_F32) epilogue_staged_f32(j, acc, stage_off);
         else epilogue_staged(j, acc, stage_off);
     };
@@ -737,16 +747,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // 1024 x 4096 GEMM ran 3.6x slower so).  The LDS word at stage_off (the
     // epilogue's staging area, free here) passes the count to all waves.
     constexpr int CP_SC1 = 16;   // cache policy of the buffer builtins: device scope
-    auto split_reduce = [&](v16f (&acc)[NB][NB], uint32_t stage_off) __attribute__((always_inline)) -> bool {
+    auto split_reduce = [&](v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) -> bool {
         const int u = my_split / split, sidx = my_split % split;
         const int ln = fresh_lane();
-        constexpr uint32_t PART = TILE * TILE * 4;   // bytes per partial tile
+        constexpr uint32_t PART = BM * BN * 4;   // bytes per partial tile
         const __amdgpu_buffer_rsrc_t rw = panel(reinterpret_cast<uint8_t*>(ws) + (size_t)my_split * PART, PART);
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NBN; ++i)
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const uint32_t off = (uint32_t)((wave * NB * NB + i * NB + jb) * 4096 + ln * 16);
+            for (int jb = 0; jb < NBM; ++jb) {
+                const uint32_t off = (uint32_t)((wave * NBN * NBM + i * NBM + jb) * 4096 + ln * 16);
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     __builtin_amdgcn_raw_buffer_store_b128(
@@ -779,10 +789,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         auto add_parts = [&](auto s_tag) __attribute__((always_inline)) {
             constexpr int S = decltype(s_tag)::value;
 #pragma unroll
-            for (int i = 0; i < NB; ++i)
+            for (int i = 0; i < NBN; ++i)
 #pragma unroll
-                for (int jb = 0; jb < NB; ++jb) {
-                    const uint32_t off = (uint32_t)((wave * NB * NB + i * NB + jb) * 4096 + ln * 16);
+                for (int jb = 0; jb < NBM; ++jb) {
+                    const uint32_t off = (uint32_t)((wave * NBN * NBM + i * NBM + jb) * 4096 + ln * 16);
                     v16f p[S];
 #pragma unroll
                     for (int s2 = 0; s2 < S; ++s2)
@@ -802,11 +812,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 
     if (nk == 0) {   // K == 0: every tile is the empty sum
         for (int j = 0; j < my_tiles; ++j) {
-            v16f acc[NB][NB];
+            v16f acc[NBN][NBM];
 #pragma unroll
-            for (int i = 0; i < NB; ++i)
+            for (int i = 0; i < NBN; ++i)
 #pragma unroll
-                for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
+                for (int jb = 0; jb < NBM; ++jb) acc[i][jb] = (v16f){};
             tile_scales_to_lds(j, 0);
             wait_vmcnt<0>();
             __syncthreads();
@@ -829,21 +839,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     }
     constexpr int PRO_ITEMS = R::PAIRED ? 4 : NSLOT - 1;   // items in flight before step 0
     for (int i = 0; i < PRO_ITEMS; ++i) {
+        const int nq = (i & 1) ? LB : LA;   // item i is operand i & 1
 #pragma unroll
-        for (int q = 0; q < LI; ++q) dma_item(q);
+        for (int q = 0; q < nq; ++q) dma_item(q);
         advance();
     }
-    wait_vmcnt<(PRO_ITEMS - 2) * LI>();
+    wait_vmcnt<loads_of(PRO_ITEMS - 2)>();
     __syncthreads();
 
     // Fragment registers are double-buffered: step t computes from one set
     // while the other receives step t+1's fragments.
-    v8i fa0[NB], fb0[NB], fa1[NB], fb1[NB];
-    uint32_t xa[NB] = {}, xb[NB] = {};
+    v8i fa0[NBM], fb0[NBN], fa1[NBM], fb1[NBN];
+    uint32_t xa[NBM] = {}, xb[NBN] = {};
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        fa0[i] = frag(0, frag_a, 0, i);
-        fb0[i] = frag(SLOT, frag_b, 0, i);
+    for (int i = 0; i < NBX; ++i) {
+        if (i < NBM) fa0[i] = frag(0, frag_a, 0, i);
+        if (i < NBN) fb0[i] = frag(SLOT, frag_b, 0, i);
     }
     read_scales(0, 0, 0, xa, xb);
     int rslot = 0;   // LDS slot of the current stage's A item (its B item is the next slot)
@@ -863,7 +874,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   LAST (the tile's last step): no reads of the next step's fragments (they
     //   are read after the epilogue, which then has their registers to itself).
     // matrix-core steps after row block 0 (12, or 2 for 128-row tiles); the
-    // step's loads and the next step's 2 NB fragment reads are spread over them.
+    // step's loads and the next step's NBM + NBN fragment reads are spread over them.
     // Mode (b) scales from LDS (once per stage, in its step 1, for the next
     // stage) are read first, in slot 0: LDS reads complete in order, so scales
     // read after the fragments would hold the next step's first matrix-core
@@ -877,14 +888,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // this step, which loads no items; with 5 slots they go first, before the
     // item loads, which the next wait may leave in flight.  Either way they
     // have landed at that wait, the earliest point the group is read.
-    constexpr int SLOTS = (NB - 1) * NB;
-    constexpr int NREAD = 2 * NB;
+    constexpr int SLOTS = (NBN - 1) * NBM;
+    constexpr int NREAD = NBM + NBN;
+    static_assert(SLOTS >= 1, "a matrix-core slot after row block 0");
     constexpr int SCALE_SLOT = R::SCALES ? 0 : (SLOTS > NREAD ? NREAD + 1 : SLOTS - 1);
-    auto kstep = [&](v16f (&acc)[NB][NB], int j, int s, auto h_tag, auto last_tag, const v8i* fa, const v8i* fb,
+    // With NSLOT >= 5 slots the ring runs NSLOT - 1 items ahead, one item per
+    // step, so step h of every stage loads an item of operand (h + NSLOT - 1) & 1
+    // (A: LA loads, B: LB).  LI_LAST: the loads of a stage's step 1 (mode (a)).
+    constexpr int LI_LAST = (NSLOT & 1) ? LB : LA;
+    auto kstep = [&](v16f (&acc)[NBN][NBM], int j, int s, auto h_tag, auto last_tag, const v8i* fa, const v8i* fb,
                      v8i* na, v8i* nbf) __attribute__((always_inline)) {
         constexpr int h = decltype(h_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
         using Ops = std::integral_constant<int, R::SCALES ? 2 * h : 0>;
+        constexpr int LI_STEP = ((h + NSLOT - 1) & 1) ? LB : LA;   // this step's loads (unpaired ring)
         // whole scale dwords are read once per stage, in its step 1 for the next stage
         constexpr bool READ_SC = !R::SCALES || h == 1;
         bool sc_go = false;
@@ -901,12 +918,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
         }
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb], Ops{});
+        for (int jb = 0; jb < NBM; ++jb) mfma(acc[0][jb], fb[0], fa[jb], xb[0], xa[jb], Ops{});
         if (h == 1) {
             __builtin_amdgcn_sched_barrier(0);
             // the next stage's items landed: with NSLOT >= 5 slots the NSLOT-4
             // items issued after them may be in flight; with 4 (paired) none
-            wait_vmcnt<(R::PAIRED ? 0 : NSLOT - 4) * LI>();
+            wait_vmcnt<R::PAIRED ? 0 : loads_of(NSLOT - 4)>();
             __syncthreads();
             // last stage of a tile: the slot of its B item is now free until the
             // next tile's first step; load the tile's scales into it for the
@@ -920,10 +937,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int sn = h ? s + 1 : s, hn = h ^ 1;
         const int na_slot = h ? slot_add(rslot, 2) : rslot;   // slots of the items read next
         const uint32_t sa_off = (uint32_t)(na_slot * SLOT), sb_off = (uint32_t)(slot_add(na_slot, 1) * SLOT);
-        uint32_t nxa[NB], nxb[NB];
+        uint32_t nxa[NBM], nxb[NBN];
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
-            const int i = 1 + k / NB, jb = k % NB;
+            const int i = 1 + k / NBM, jb = k % NBM;
             mfma(acc[i][jb], fb[i], fa[jb], xb[i], xa[jb], Ops{});
             if constexpr (R::SCALES) {
                 if (sc_go) {
@@ -939,23 +956,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             }
             if constexpr (!R::PAIRED) {
 #pragma unroll
-                for (int q = share_lo(k, LI, SLOTS); q < share_hi(k, LI, SLOTS); ++q) dma_item(q);
+                for (int q = share_lo(k, LI_STEP, SLOTS); q < share_hi(k, LI_STEP, SLOTS); ++q) dma_item(q);
             } else if (h == 1) {
                 // the stage's two items: the first over the first half of the slots, the second over the rest
                 constexpr int HALF = SLOTS / 2;
                 const int kk = k % HALF;
 #pragma unroll
-                for (int q = kk * LI / HALF; q < (kk + 1) * LI / HALF; ++q) dma_item(q);
+                for (int q = kk * LA / HALF; q < (kk + 1) * LA / HALF; ++q) dma_item(q);
                 if (k == HALF - 1) advance();
             }
-            // reads in order of first use: row block 0 of B, the NB of A, then the rest of B
+            // reads in order of first use: row block 0 of B, the NBM of A, then the rest of B
             if constexpr (!LAST) {
                 if (R::SCALES && READ_SC && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
 #pragma unroll
                 for (int e = share_lo(k, NREAD, SLOTS); e < share_hi(k, NREAD, SLOTS); ++e) {
                     if (e == 0) nbf[0] = frag(sb_off, frag_b, hn, 0);
-                    else if (e <= NB) na[e - 1] = frag(sa_off, frag_a, hn, e - 1);
-                    else nbf[e - NB] = frag(sb_off, frag_b, hn, e - NB);
+                    else if (e <= NBM) na[e - 1] = frag(sa_off, frag_a, hn, e - 1);
+                    else nbf[e - NBM] = frag(sb_off, frag_b, hn, e - NBM);
                 }
                 if (!R::SCALES && k == SCALE_SLOT) read_scales(j, sn, hn, nxa, nxb);
             }
@@ -965,12 +982,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         if (h) rslot = na_slot;
         // keep this step's operand registers allocated to its end
 #pragma unroll
-        for (int i = 0; i < NB; ++i) asm volatile("" : : "v"(fa[i]), "v"(fb[i]));
+        for (int i = 0; i < NBX; ++i) {
+            if (i < NBM && i < NBN) asm volatile("" : : "v"(fa[i]), "v"(fb[i]));
+            else if (i < NBM) asm volatile("" : : "v"(fa[i]));
+            else asm volatile("" : : "v"(fb[i]));
+        }
         if constexpr (!LAST && READ_SC) {
 #pragma unroll
-            for (int i = 0; i < NB; ++i) {
-                xa[i] = nxa[i];
-                xb[i] = nxb[i];
+            for (int i = 0; i < NBX; ++i) {
+                if (i < NBM) xa[i] = nxa[i];
+                if (i < NBN) xb[i] = nxb[i];
             }
         }
     };
@@ -980,11 +1001,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     using Last = std::integral_constant<bool, true>;
 
     for (int j = 0; j < my_tiles; ++j) {
-        v16f acc[NB][NB];   // [n block][m block]
+        v16f acc[NBN][NBM];   // [n block][m block]
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
+        for (int i = 0; i < NBN; ++i)
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) acc[i][jb] = (v16f){};
+            for (int jb = 0; jb < NBM; ++jb) acc[i][jb] = (v16f){};
         const int nsj = SPLIT ? item_of(j).ns : nk;   // stages of this work item
         for (int s = 0; s < nsj - 1; ++s) {
             kstep(acc, j, s, Step0{}, NotLast{}, fa0, fb0, fa1, fb1);
@@ -1001,13 +1022,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             if (j == my_whole && !split_reduce(acc, stage_off)) break;
         }
         if (staged) {
-            if constexpr (!MX) wait_vmcnt<LI>();   // the tile's scales (only the last item's loads may be in flight)
+            if constexpr (!MX) wait_vmcnt<LI_LAST>();   // the tile's scales (only the last item's loads may be in flight)
             __syncthreads();
             epilogue_staged_any(j, acc, stage_off);
             __syncthreads();   // staging reads done before that slot is loaded again
         } else {
             if constexpr (!MX) {
-                wait_vmcnt<LI>();
+                wait_vmcnt<LI_LAST>();
                 __syncthreads();
             }
             epilogue(j, acc, stage_off);
@@ -1019,9 +1040,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         // (LDS) are harmless and unused; the scales are read only for a tile
         // that exists (the K-tail path reads them from global memory).
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            fa0[i] = frag((uint32_t)(rslot * SLOT), frag_a, 0, i);
-            fb0[i] = frag((uint32_t)(slot_add(rslot, 1) * SLOT), frag_b, 0, i);
+        for (int i = 0; i < NBX; ++i) {
+            if (i < NBM) fa0[i] = frag((uint32_t)(rslot * SLOT), frag_a, 0, i);
+            if (i < NBN) fb0[i] = frag((uint32_t)(slot_add(rslot, 1) * SLOT), frag_b, 0, i);
         }
         if (j + 1 < my_tiles) read_scales(j + 1, 0, 0, xa, xb);
     }
@@ -1048,18 +1069,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 struct SplitPlan {
     int tiles_whole, split;
 };
+constexpr double T_STAGE_US = 0.37, T_FIXED_US = 1.5, BYTES_PER_US = 4.0e6;
+constexpr double PART_BYTES = 128.0 * 128.0 * 4.0;
+// predicted K loop and exchange of r tiles of nk stages split s ways
+static double split_us(int64_t r, int s, int64_t nk) {
+    const double moved = (double)(s * r) * PART_BYTES * (1.0 + (double)(s - 1) / s);
+    return (double)(nk / s) * T_STAGE_US + T_FIXED_US + moved / BYTES_PER_US;
+}
 static SplitPlan split_plan(int64_t tiles, int cus, int64_t nk) {
-    constexpr double T_STAGE_US = 0.37, T_FIXED_US = 1.5, BYTES_PER_US = 4.0e6;
-    constexpr double PART_BYTES = 128.0 * 128.0 * 4.0;
     SplitPlan p{(int)tiles, 1};
     const int64_t r = tiles % cus;
     if (r == 0 || 2 * r > cus || nk < 8) return p;
     double best = 0.1 * (double)nk * T_STAGE_US;   // require a predicted gain of 10% at least
     for (int s = 2; s <= 4 && s <= cus / r; ++s) {
         if (nk % s != 0 || nk / s < 4) continue;
-        const double saved = (double)(nk - nk / s) * T_STAGE_US;
-        const double moved = (double)(s * r) * PART_BYTES * (1.0 + (double)(s - 1) / s);
-        const double gain = saved - (T_FIXED_US + moved / BYTES_PER_US);
+        const double gain = (double)nk * T_STAGE_US - split_us(r, s, nk);
         if (gain > best) {
             best = gain;
             p.split = s;
@@ -1067,6 +1091,22 @@ static SplitPlan split_plan(int64_t tiles, int cus, int64_t nk) {
         }
     }
     return p;
+}
+// 64x128 tiles or 128x128 tiles split over K, for a problem whose 128x128
+// tiles fill at most half of the CUs (so its 64x128 tiles fit one round):
+// a stage of a round of 64x128 tiles takes about 0.30 us (measured at K =
+// 1024 .. 8192 with 128 and 256 tiles), against the split schedule's
+// predicted loop and exchange; 64x128 tiles are taken when they are predicted
+// at least 5% faster (the model's error on the shapes measured).  Measured,
+// split / 64x128 tiles: 1024x1024x4096 16.0 / 14.6 us; 512x2048x4096 16.1 /
+// 14.8 us; 2048x1024x8192 23.9 / 24.8 us; 1024x1024x8192 20.5 / 24.6 us;
+// 512x512x8192 16.2 / 24.6 us; 128x128x4096 12.6 / 14.3 us.
+static bool prefer_tile64(int64_t tiles128, int cus, int64_t nk, bool tail) {
+    constexpr double T64_STAGE_US = 0.30;
+    if (tail) return true;
+    const SplitPlan sp = split_plan(tiles128, cus, nk);
+    if (sp.split == 1) return true;
+    return (double)nk * T64_STAGE_US < 0.95 * split_us(tiles128 - sp.tiles_whole, sp.split, nk);
 }
 static int64_t ws_cnt_bytes(int cus) { return ((int64_t)cus * 4 + 255) / 256 * 256; }
 // bytes of workspace any split launch on a device with `cus` CUs may use
@@ -1134,7 +1174,8 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
         if (e != hipSuccess) return e;
         configured.fetch_or(bit, std::memory_order_release);
     }
-    const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
+    constexpr int BM = Geo<TILE>::BM, BN = Geo<TILE>::BN;
+    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     const int64_t items = SPLIT ? sp.tiles_whole + (tiles - sp.tiles_whole) * sp.split : tiles;
     const int64_t grid = items < cus ? items : cus;   // persistent: at most one workgroup per CU
     int* cnt = SPLIT ? reinterpret_cast<int*>(ws) : nullptr;
@@ -1151,7 +1192,8 @@ static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
-    const int64_t tiles = ((m + TILE - 1) / TILE) * ((n + TILE - 1) / TILE);
+    constexpr int BM = Geo<TILE>::BM, BN = Geo<TILE>::BN;
+    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
     if constexpr (!MX && TILE == 128) {   // (256-row tiles: the split kernel would spill around its last step)
         const SplitPlan sp = split_plan(tiles, cus, k / BK);
         if (!tail && sp.split > 1) {
@@ -1196,8 +1238,18 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     // were 4-35% faster.
     const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
     const bool spill = !MX && tiles256 > cus && 8 * (tiles256 - cus) <= cus;
-    if (2 * tiles256 <= cus || spill)
+    if (2 * tiles256 <= cus || spill) {
+        if constexpr (!MX) {
+            // 64x128 tiles (mode (a)) when 128x128 tiles would leave at least
+            // half of the CUs idle and are not split over K: twice the
+            // workgroups, each with half the matrix-core work per stage
+            const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
+            if (!spill && 2 * tiles128 <= cus && prefer_tile64(tiles128, cus, k / BK, (k % BK) != 0))
+                return launch_tiled<MX, FA, FB, 64>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws,
+                                                    stream);
+        }
         return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
+    }
     return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
 }
 

@@ -56,19 +56,22 @@ def uscale(seed, n, stream=3):
 
 
 # (M, N, K): tile-aligned, ragged in m/n, a K tail that is not a multiple of the
-# 128-byte stage, single elements, several tiles in both directions.  Problems
-# with at most half as many 256x256 tiles as CUs run on 128x128 tiles; 2561 x
-# 3000 (11 x 12 tiles of 256) and larger take the 256x256 kernels, with ragged
-# m, n and a K tail.  The epilogue depends on N: bf16 is staged through LDS for
-# N % 8 == 0, fp32 for N % 32 == 0 (1000 x 1024, 2600 x 3072, 2561 x 3008);
-# other N store from registers.  4864 x 4096 and 4864 x 4032 have 304 tiles
-# of 256 for 256 workgroups: a workgroup runs a second tile, so its epilogue
-# borrows a ring slot while the next tile's loads are in flight.  4352 x 4096
-# (272 tiles of 256, just past one round) runs on 1088 tiles of 128.
+# 128-byte stage, single elements, several tiles in both directions.  On a
+# 256-CU part: problems whose 128x128 tiles would fill at most half of the CUs
+# (and are not split over K) run on 64x128 tiles, every shape here up to
+# 1000 x 1024; 1900 x 2000 (240 tiles of 128) and 2048 x 2048 (256) run on
+# 128x128 tiles; 2561 x 3000 (11 x 12 tiles of 256) and larger take the
+# 256x256 kernels, with ragged m, n and a K tail.  The epilogue depends on N:
+# bf16 is staged through LDS for N % 8 == 0, fp32 for N % 32 == 0 (1000 x
+# 1024, 2048 x 2048, 2600 x 3072, 2561 x 3008); other N store from registers.
+# 4864 x 4096 and 4864 x 4032 have 304 tiles of 256 for 256 workgroups: a
+# workgroup runs a second tile, so its epilogue borrows a ring slot while the
+# next tile's loads are in flight.  4352 x 4096 (272 tiles of 256, just past
+# one round) runs on 1088 tiles of 128.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
-            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (2561, 3000, 272),
-            (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024), (4864, 4096, 256), (4864, 4032, 272),
-            (4352, 4096, 272)]
+            (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (1900, 2000, 1024),
+            (2048, 2048, 256), (2561, 3000, 272), (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024),
+            (4864, 4096, 256), (4864, 4032, 272), (4352, 4096, 272)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -100,16 +103,18 @@ def test_mode_a_raw_cast_workloads(gpu_lib, name, out):
 
 
 # Shapes whose last round of 128x128 tiles is at most half full, with K long
-# enough for the split to pay, split those tiles over K (S = 2 or 4 items per
-# tile; the last item to finish adds the partials in split order and stores
-# the tile): no whole rounds (128x128x4096: one tile in 4 items; 512x512x8192,
-# 1024x1024x4096, 2048x1024x8192), ragged m and n with the epilogue from
-# registers (1000x1001x8192, N % 8 != 0) or staged (1000x1024x8192), and
-# whole rounds before a split tail (4352x4096x8192: 1024 whole tiles, then 64
-# tiles in 4 items).  Each shape runs three times: the per-tile counters must
-# be back at zero after every launch for the next to add up the same.
-SHAPES_SPLIT = [(128, 128, 4096), (512, 512, 8192), (1000, 1001, 8192), (1000, 1024, 8192), (1024, 1024, 4096),
-                (2048, 1024, 8192), (4352, 4096, 8192)]
+# enough for the split to pay (and, when the 128x128 tiles fill at most half
+# of the CUs, to beat 64x128 tiles), split those tiles over K (S = 2 or 4
+# items per tile; the last item to finish adds the partials in split order
+# and stores the tile): no whole rounds (128x128x4096: one tile in 4 items;
+# 512x512x8192, 1024x1024x8192, 1024x512x4096, 2048x512x8192), ragged m and n
+# with the epilogue from registers (1000x1001x8192, N % 8 != 0) or staged
+# (1000x1024x8192), and whole rounds before a split tail (4352x4096x8192: 1024
+# whole tiles, then 64 tiles in 4 items).  Each shape runs three times: the
+# per-tile counters must be back at zero after every launch for the next to
+# add up the same.
+SHAPES_SPLIT = [(128, 128, 4096), (512, 512, 8192), (1000, 1001, 8192), (1000, 1024, 8192), (1024, 1024, 8192),
+                (1024, 512, 4096), (2048, 512, 8192), (4352, 4096, 8192)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -136,10 +141,11 @@ def test_mode_a_split_k(gpu_lib, M, N, K, out):
 
 
 # k = 0: every output is the empty sum.  The shapes take each epilogue path:
-# from registers (N = 90), staged through LDS on 128-row tiles (300 x 512) and
-# on 256-row tiles (2600 x 3072), for both output types.
+# from registers (N = 90), staged through LDS on 64x128 tiles (300 x 512), on
+# 128x128 tiles (2048 x 2048) and on 256x256 tiles (2600 x 3072), for both
+# output types.
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-@pytest.mark.parametrize("M,N", [(70, 90), (300, 512), (2600, 3072)])
+@pytest.mark.parametrize("M,N", [(70, 90), (300, 512), (2048, 2048), (2600, 3072)])
 def test_mode_a_k_zero(gpu_lib, M, N, out):
     import torch
     A = torch.empty((M, 0), dtype=torch.uint8, device="cuda")

@@ -30,7 +30,7 @@ def _call(lib, name, M, N, K, A, B, sa, sb, D, out):
 
 
 # 512x512x8192: 16 tiles of 128, each split into 4 K ranges; 128x128x4096: one
-# tile in 4; 1000x1001x272: no split (K tail)
+# tile in 4; 1000x1001x272: no split (K tail; 64x128 tiles)
 @pytest.mark.parametrize("out", [0, 1])
 def test_noalloc_matches_fp8_gemm_scaled(gpu_lib, out):
     import torch
