@@ -122,7 +122,7 @@ struct Ring {
     using G = Geo<TILE>;
     static_assert(!MX || G::BM == G::BN, "mode (b): square tiles");
     static constexpr bool SCALES = MX && !KTAIL;
-    static constexpr int NSLOT = TILE == 256 ? (SCALES ? 4 : 5) : (MX ? 5 : 8);
+    static constexpr int NSLOT = TILE == 256 ? (SCALES ? 4 : 5) : TILE == 64 ? 6 : (MX ? 5 : 8);
     static constexpr int SLOT = G::B_BYTES > G::A_BYTES ? G::B_BYTES : G::A_BYTES;
     static constexpr int LDS = NSLOT * SLOT;
     static constexpr int LA = G::LA, LB = G::LB;   // load instructions per item and wave, A and B
@@ -1093,20 +1093,18 @@ static SplitPlan split_plan(int64_t tiles, int cus, int64_t nk) {
     return p;
 }
 // 64x128 tiles or 128x128 tiles split over K, for a problem whose 128x128
-// tiles fill at most half of the CUs (so its 64x128 tiles fit one round):
-// a stage of a round of 64x128 tiles takes about 0.30 us (measured at K =
-// 1024 .. 8192 with 128 and 256 tiles), against the split schedule's
-// predicted loop and exchange; 64x128 tiles are taken when they are predicted
-// at least 5% faster (the model's error on the shapes measured).  Measured,
-// split / 64x128 tiles: 1024x1024x4096 16.0 / 14.6 us; 512x2048x4096 16.1 /
-// 14.8 us; 2048x1024x8192 23.9 / 24.8 us; 1024x1024x8192 20.5 / 24.6 us;
-// 512x512x8192 16.2 / 24.6 us; 128x128x4096 12.6 / 14.3 us.
+// tiles fill at most half of the CUs (so its 64x128 tiles fit one round).
+// Fitted to measurements on MI355X: one round of 64x128 tiles takes about
+// 4.4 us plus 0.26 us per stage, one of 128x128 tiles 5.4 us plus the split
+// schedule's predicted loop and exchange; 64x128 tiles are taken when they
+// are predicted at least 5% faster.
 static bool prefer_tile64(int64_t tiles128, int cus, int64_t nk, bool tail) {
-    constexpr double T64_STAGE_US = 0.30;
+    constexpr double T64_FIXED_US = 4.4, T64_STAGE_US = 0.26, T128_FIXED_US = 5.4;
     if (tail) return true;
     const SplitPlan sp = split_plan(tiles128, cus, nk);
     if (sp.split == 1) return true;
-    return (double)nk * T64_STAGE_US < 0.95 * split_us(tiles128 - sp.tiles_whole, sp.split, nk);
+    return T64_FIXED_US + (double)nk * T64_STAGE_US <
+           0.95 * (T128_FIXED_US + split_us(tiles128 - sp.tiles_whole, sp.split, nk));
 }
 static int64_t ws_cnt_bytes(int cus) { return ((int64_t)cus * 4 + 255) / 256 * 256; }
 // bytes of workspace any split launch on a device with `cus` CUs may use

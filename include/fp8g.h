@@ -146,7 +146,8 @@ int fp8_quantize_rowwise(const float* x, int64_t rows, int64_t cols,
  * D        device, [m, n] of out_dtype (fp8g_out_t), written
  * m, n, k >= 0.  m == 0 or n == 0: no-op.  k == 0: D = 0.
  * Split workspace: when the 128x128 output tiles leave a last round of tiles
- * at most half full and K (a multiple of 128) is long enough to pay, those
+ * at most half full and K (a multiple of 128) is long enough to pay (and, for
+ * problems whose 64x128 tiles fit one round, pays more than those), those
  * tiles are split over K and their partial sums pass through a device
  * workspace (with per-tile counters).  The library allocates it with
  * hipMalloc (64 MB + 1 KB on a 256-CU device) on the first such call on each
