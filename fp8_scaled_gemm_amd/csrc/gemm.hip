@@ -20,9 +20,12 @@
 // Tiling: a 256-thread workgroup (4 waves, 2x2) owns a 256x256 output tile;
 // each wave owns 128x128 = 4x4 blocks of the 32x32 matrix-core tile (256 fp32
 // accumulators per lane).  Problems with at most half as many 256x256 tiles as
-// CUs (2048 x 1024: 32 tiles for 256 CUs) use 128x128 tiles instead (waves of
-// 64x64 = 2x2 blocks): four times the workgroups, each moving twice the
-// operand bytes per flop, which the idle CUs more than pay for.
+// CUs use 128x128 tiles instead (waves of 64x64 = 2x2 blocks): four times the
+// workgroups, each moving twice the operand bytes per flop, which the idle
+// CUs more than pay for.  In mode (a), problems whose 128x128 tiles would
+// still fill at most half of the CUs (2048 x 1024: 128 tiles for 256 CUs) use
+// 64x128 tiles (waves of 32x64 = 1x2 blocks), unless splitting the 128x128
+// tiles over K is predicted faster.
 //
 // K is walked in 64-byte steps, one V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block
 // per step; mode (a) passes the neutral scale code 127 (2^0) and applies sa,
@@ -116,7 +119,11 @@ struct Geo {
 // LDS, so mode (b) with whole scale dwords (scale groups beside the ring)
 // fits only 4 slots.  128-row items: mode (a) 8 slots of 16 KB, loads 7 items
 // ahead (against 5 slots: 7-10% faster at 2048x1024x4096 and the other
-// 128-tile shapes measured); mode (b) 5 (8 slots ran 5% slower there).
+// 128-tile shapes measured; 6 or 7 slots: the same within 2%); mode (b) 5
+// (8 slots ran 5% slower there).  64x128 tiles (A items of 8 KB in slots of
+// 16 KB): 6 slots, loads 5 items ahead (at 2048x1024x4096: 13.0 us, against
+// 16.8 us with 5 slots, 15.0 us with 8 and 16.4 us with 10 slots of 24 KB
+// pairs).
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
     using G = Geo<TILE>;
@@ -873,7 +880,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     //   matrix-core steps behind a burst of loads from all four waves.
     //   LAST (the tile's last step): no reads of the next step's fragments (they
     //   are read after the epilogue, which then has their registers to itself).
-    // matrix-core steps after row block 0 (12, or 2 for 128-row tiles); the
+    // matrix-core steps after row block 0 (12, 2 for 128x128 and 1 for 64x128 tiles); the
     // step's loads and the next step's NBM + NBN fragment reads are spread over them.
     // Mode (b) scales from LDS (once per stage, in its step 1, for the next
     // stage) are read first, in slot 0: LDS reads complete in order, so scales
@@ -1063,7 +1070,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 // 128x128x4096 16.7 -> 12.2 us (S = 4), 2048x1024x8192 31.2 -> 26.3 us
 // (S = 2), 1024x1024x4096 17.1 -> 15.9 us (S = 4); 2048x1024x4096 gained
 // nothing (18.2 / 18.4 us: 16 stages saved, 24 MB exchanged) and
-// 2048x1024x1024 lost 44%, so neither splits.  The workspace holds the arrival
+// 2048x1024x1024 lost 44%, so neither splits.  (Those two and 1024x1024x4096
+// now run on 64x128 tiles; see prefer_tile64.)  The workspace holds the arrival
 // counters (one int per split tile, padded to 256 bytes) and the partial
 // tiles (S r <= CUs of them).
 struct SplitPlan {
@@ -1097,7 +1105,12 @@ static SplitPlan split_plan(int64_t tiles, int cus, int64_t nk) {
 // Fitted to measurements on MI355X: one round of 64x128 tiles takes about
 // 4.4 us plus 0.26 us per stage, one of 128x128 tiles 5.4 us plus the split
 // schedule's predicted loop and exchange; 64x128 tiles are taken when they
-// are predicted at least 5% faster.
+// are predicted at least 5% faster.  Measured (split / 64x128 tiles):
+// 1024x1024x8192 21.2 / 23.0 us, 512x512x8192 16.0 / 20.8 us, 256x256x16384
+// 22.0 / 37.6 us (split taken); 2048x1024x8192 27.1 / 25.2 us, 1024x512x4096
+// 13.7 / 12.3 us (64x128 taken).  The model misses the smallest problems by
+// a few percent: 128x128x4096 12.9 / 12.1 us and 1024x256x4096 13.0 /
+// 12.3 us take the split.
 static bool prefer_tile64(int64_t tiles128, int cus, int64_t nk, bool tail) {
     constexpr double T64_FIXED_US = 4.4, T64_STAGE_US = 0.26, T128_FIXED_US = 5.4;
     if (tail) return true;
