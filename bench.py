@@ -114,45 +114,63 @@ def copy_only(nbytes, reps=5):
     print(json.dumps({"copy_bytes": nbytes, "seconds": dt, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}))
 
 
+CPU_MIN_S = 10.0   # the oracle's sample is repeated until it has run this long
+
+
+def _repeat(fn, min_s=CPU_MIN_S):
+    """Run fn until min_s seconds have passed: (runs, seconds)."""
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        fn()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return runs, dt
+
+
 def cpu_baseline_ffn_up(w, m_s=4096, n_s=16384, fa="e4m3", fb="e4m3"):
     """The oracle on a sample: rows 0..m_s of the activations, rows 0..n_s of the
-    weights: quantize both (row-wise) and form the m_s x n_s block of D."""
+    weights: quantize both (row-wise) and form the m_s x n_s block of D,
+    repeated until CPU_MIN_S seconds have passed."""
     from oracle import gemm, quant
     XA = synth.draw(w, "a", slice(0, m_s))
     XB = synth.draw(w, "b", slice(0, n_s))
-    t0 = time.perf_counter()
-    qa = np.empty(XA.shape, np.uint8)
-    qb = np.empty(XB.shape, np.uint8)
-    sa = np.empty(m_s, np.float32)
-    sb = np.empty(n_s, np.float32)
-    for r in range(0, m_s, 256):
-        qa[r:r + 256], sa[r:r + 256] = quant.quantize_rowwise(XA[r:r + 256], fa)
-    for r in range(0, n_s, 256):
-        qb[r:r + 256], sb[r:r + 256] = quant.quantize_rowwise(XB[r:r + 256], fb)
-    gemm.gemm_scaled(qa, qb, sa, sb, fa, fb)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * m_s * n_s * w.K
+
+    def once():
+        qa = np.empty(XA.shape, np.uint8)
+        qb = np.empty(XB.shape, np.uint8)
+        sa = np.empty(m_s, np.float32)
+        sb = np.empty(n_s, np.float32)
+        for r in range(0, m_s, 256):
+            qa[r:r + 256], sa[r:r + 256] = quant.quantize_rowwise(XA[r:r + 256], fa)
+        for r in range(0, n_s, 256):
+            qb[r:r + 256], sb[r:r + 256] = quant.quantize_rowwise(XB[r:r + 256], fb)
+        gemm.gemm_scaled(qa, qb, sa, sb, fa, fb)
+    runs, dt = _repeat(once)
+    flops = 2.0 * m_s * n_s * w.K * runs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "runs": runs,
             "sample": "oracle row-wise quantize of activation rows 0..%d and weight rows 0..%d, then the "
-                      "%dx%dx%d block of D in float64 (numpy matmul); value = 2*%d*%d*%d flops / time"
-                      % (m_s, n_s, m_s, n_s, w.K, m_s, n_s, w.K)}
+                      "%dx%dx%d block of D in float64 (numpy matmul), %d time(s); value = 2*%d*%d*%d flops "
+                      "per run / time" % (m_s, n_s, m_s, n_s, w.K, runs, m_s, n_s, w.K)}
 
 
 def cpu_baseline_mx(w, m_s=2048, n_s=8192):
     from oracle import gemm, quant
     XA = synth.draw(w, "a", slice(0, m_s))
     XB = synth.draw(w, "b", slice(0, n_s))
-    t0 = time.perf_counter()
-    qa, ea = quant.mx_quantize(XA)
-    qb, eb = quant.mx_quantize(XB)
-    gemm.mxfp8_gemm(qa, qb, ea, eb)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * m_s * n_s * w.K
+
+    def once():
+        qa, ea = quant.mx_quantize(XA)
+        qb, eb = quant.mx_quantize(XB)
+        gemm.mxfp8_gemm(qa, qb, ea, eb)
+    runs, dt = _repeat(once)
+    flops = 2.0 * m_s * n_s * w.K * runs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": "oracle MX quantize of rows 0..%d / 0..%d, then the %dx%dx%d block of D in float64"
-                      % (m_s, n_s, m_s, n_s, w.K)}
+            "seconds": round(dt, 3), "runs": runs,
+            "sample": "oracle MX quantize of rows 0..%d / 0..%d, then the %dx%dx%d block of D in float64, "
+                      "%d time(s)" % (m_s, n_s, m_s, n_s, w.K, runs)}
 
 
 TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic.txt",
@@ -406,13 +424,15 @@ def cpu_baseline_c2(w):
     from oracle import e4m3, gemm
     XA, XB = synth.draw(w, "a"), synth.draw(w, "b")
     sa, sb = synth.scales(w, "a"), synth.scales(w, "b")
-    t0 = time.perf_counter()
-    qa, qb = e4m3.encode(XA), e4m3.encode(XB)
-    gemm.gemm_scaled(qa, qb, sa, sb)
-    dt = time.perf_counter() - t0
-    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": "the whole workload: oracle E4M3 cast of A and B, then all of D in float64 (numpy matmul)"}
+
+    def once():
+        qa, qb = e4m3.encode(XA), e4m3.encode(XB)
+        gemm.gemm_scaled(qa, qb, sa, sb)
+    runs, dt = _repeat(once)
+    return {"value": w.flops * runs / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "seconds": round(dt, 3), "runs": runs,
+            "sample": "the whole workload: oracle E4M3 cast of A and B, then all of D in float64 (numpy "
+                      "matmul), %d time(s)" % runs}
 
 
 def gemm_only_bench(args, torch, fp8g, w):
