@@ -59,6 +59,8 @@ _SIGNATURES = {
     "mxfp8_gemm_ex": [_I64, _I64, _I64, _VOIDP, ctypes.c_int, _VOIDP, ctypes.c_int, _VOIDP, _VOIDP, _VOIDP,
                       ctypes.c_int, _VOIDP],
     "concat_mla_k": [_VOIDP, _VOIDP, _VOIDP, _I64, _I64, _I64, ctypes.c_int, _VOIDP],
+    "fp8g_gemm_schedule": [_I64, _I64, _I64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)],
     "fp8g_roof_mfma": [_I64, _I64, _VOIDP, _VOIDP],
     "fp8g_roof_stream": [_VOIDP, _I64, _VOIDP, ctypes.c_int, ctypes.c_int, _VOIDP],
 }
@@ -356,6 +358,20 @@ def concat_mla_k(k_nope, k_rope, k=None):
     _check(load().concat_mla_k(_ptr(k), _ptr(k_nope), _ptr(k_rope), T, H, k_rope.shape[1], esz, _stream()),
            "concat_mla_k")
     return k
+
+
+def fp8g_gemm_schedule(m, n, k, mode=0, cus=None):
+    """The schedule a GEMM launch takes for m x n x k on a device with `cus`
+    compute units (default: the current device's): mode 0 = fp8_gemm_scaled,
+    1 = mxfp8_gemm.  Host only.  Returns a dict with tile_m, tile_n, split
+    (1: no K split) and split_tiles."""
+    if cus is None:
+        torch = _torch()
+        cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = [ctypes.c_int(0) for _ in range(4)]
+    _check(load().fp8g_gemm_schedule(int(m), int(n), int(k), int(mode), int(cus), *[ctypes.byref(o) for o in out]),
+           "fp8g_gemm_schedule")
+    return dict(zip(("tile_m", "tile_n", "split", "split_tiles"), (o.value for o in out)))
 
 
 def fp8g_roof_mfma(blocks, iters, sink=None):

@@ -175,6 +175,16 @@ int concat_mla_k(void* k, const void* k_nope, const void* k_rope, int64_t tokens
     return hip_status(fp8g::launch_concat_mla_k(k, k_nope, k_rope, tokens, heads, rope_heads, elem_bytes, stream));
 }
 
+int fp8g_gemm_schedule(int64_t m, int64_t n, int64_t k, int mode, int cus, int* tile_m, int* tile_n, int* split,
+                       int* split_tiles) {
+    if (m < 0 || n < 0 || k < 0 || cus < 1) return FP8G_ERR_SHAPE;
+    if (mode != 0 && mode != 1) return FP8G_ERR_DTYPE;
+    if (!tile_m || !tile_n || !split || !split_tiles) return FP8G_ERR_NULL;
+    if (fp8g::schedule_gemm(m, n, k, mode, cus, tile_m, tile_n, split, split_tiles) != hipSuccess)
+        return FP8G_ERR_UNSUPPORTED;
+    return FP8G_OK;
+}
+
 int fp8g_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t stream) {
     if (blocks < 1 || iters < 1 || blocks >= ((int64_t)1 << 31) || iters >= ((int64_t)1 << 31)) return FP8G_ERR_SHAPE;
     if (!sink) return FP8G_ERR_NULL;

@@ -1196,17 +1196,53 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
     return hipGetLastError();
 }
 
+// The schedule of a launch on a device with `cus` CUs: the tile shape and,
+// for 128x128 tiles in mode (a) with K a multiple of 128, the split plan.  The
+// launch and fp8g_gemm_schedule both take it from here.
+//   128x128 tiles when 256x256 tiles would leave at least half of the CUs
+//   idle: four times the tiles, each at a lower matrix-core rate.  Mode (a)
+//   also when the 256x256 tiles spill just past one round (at most an eighth
+//   of a second one): 4352x4096 (272 tiles) ran 4-14% faster on 128x128 tiles
+//   at K = 1024..8192, while at 1.5 and 2 rounds the 256x256 tiles were
+//   4-35% faster.
+//   64x128 tiles (mode (a)) when 128x128 tiles would leave at least half of
+//   the CUs idle and splitting them over K is not predicted faster
+//   (prefer_tile64): twice the workgroups, each with half the matrix-core
+//   work per stage.
+//   Only 128x128 tiles split: the 256x256 split kernel would spill around its
+//   last step.
+struct Schedule {
+    int tile;       // 256, 128 or 64 (64x128)
+    SplitPlan sp;   // split == 1: no split
+};
+static Schedule gemm_schedule(int64_t m, int64_t n, int64_t k, bool mx, int cus) {
+    const bool tail = (k % BK) != 0;
+    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
+    const bool spill = !mx && tiles256 > cus && 8 * (tiles256 - cus) <= cus;
+    if (2 * tiles256 <= cus || spill) {
+        const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
+        if (!mx) {
+            if (!spill && 2 * tiles128 <= cus && prefer_tile64(tiles128, cus, k / BK, tail)) {
+                const int64_t tiles64 = ((m + 63) / 64) * ((n + 127) / 128);
+                return {64, {(int)tiles64, 1}};
+            }
+            if (!tail) return {128, split_plan(tiles128, cus, k / BK)};
+        }
+        return {128, {(int)tiles128, 1}};
+    }
+    return {256, {(int)tiles256, 1}};
+}
+
 template <bool MX, int FA, int FB, int TILE>
 static hipError_t launch_tiled(int64_t m, int64_t n, int64_t k, const uint8_t* A, const uint8_t* B, const float* sa,
                                const float* sb, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32, int dev,
-                               int cus, void* fixed_ws, hipStream_t stream) {
+                               int cus, const SplitPlan& sp, void* fixed_ws, hipStream_t stream) {
     // a K tail (k not a multiple of the 128-byte stage) zero-fills the bytes
     // past K and, in mode (b), reads the scales byte by byte from global memory
     const bool tail = (k % BK) != 0;
     constexpr int BM = Geo<TILE>::BM, BN = Geo<TILE>::BN;
     const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    if constexpr (!MX && TILE == 128) {   // (256-row tiles: the split kernel would spill around its last step)
-        const SplitPlan sp = split_plan(tiles, cus, k / BK);
+    if constexpr (!MX && TILE == 128) {
         if (!tail && sp.split > 1) {
             void* ws = fixed_ws;   // the caller's fixed workspace (of split_ws_bytes(cus) at least), or the stream's
             if (!ws) {
@@ -1241,27 +1277,16 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    // 128-row tiles when 256-row tiles would leave at least half of the CUs
-    // idle: four times the tiles, each at a lower matrix-core rate.  Mode (a)
-    // also when the 256-row tiles spill just past one round (at most an eighth
-    // of a second one): 4352x4096 (272 tiles) ran 4-14% faster on 128-row
-    // tiles at K = 1024..8192, while at 1.5 and 2 rounds the 256-row tiles
-    // were 4-35% faster.
-    const int64_t tiles256 = ((m + 255) / 256) * ((n + 255) / 256);
-    const bool spill = !MX && tiles256 > cus && 8 * (tiles256 - cus) <= cus;
-    if (2 * tiles256 <= cus || spill) {
-        if constexpr (!MX) {
-            // 64x128 tiles (mode (a)) when 128x128 tiles would leave at least
-            // half of the CUs idle and are not split over K: twice the
-            // workgroups, each with half the matrix-core work per stage
-            const int64_t tiles128 = ((m + 127) / 128) * ((n + 127) / 128);
-            if (!spill && 2 * tiles128 <= cus && prefer_tile64(tiles128, cus, k / BK, (k % BK) != 0))
-                return launch_tiled<MX, FA, FB, 64>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws,
-                                                    stream);
-        }
-        return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
+    const Schedule sc = gemm_schedule(m, n, k, MX, cus);
+    if constexpr (!MX) {
+        if (sc.tile == 64)
+            return launch_tiled<MX, FA, FB, 64>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws,
+                                                stream);
     }
-    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, fixed_ws, stream);
+    if (sc.tile == 128)
+        return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws,
+                                             stream);
+    return launch_tiled<MX, FA, FB, 256>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws, stream);
 }
 
 // Each operand-format pair's kernels may be compiled in an object of their
@@ -1314,6 +1339,18 @@ static hipError_t launch_mode(int64_t m, int64_t n, int64_t k, const uint8_t* A,
 static bool fits(int64_t m, int64_t n, int64_t k) {
     const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
     return m < (1LL << 31) && n < (1LL << 31) && k < (1LL << 23) && tiles < (1LL << 31);
+}
+
+hipError_t schedule_gemm(int64_t m, int64_t n, int64_t k, int mx, int cus, int* tile_m, int* tile_n, int* split,
+                         int* split_tiles) {
+    if (!fits(m, n, k)) return hipErrorInvalidValue;
+    const Schedule sc = gemm_schedule(m, n, k, mx != 0, cus);
+    *tile_m = sc.tile;
+    *tile_n = sc.tile == 64 ? 128 : sc.tile;
+    *split = sc.sp.split;
+    const int64_t tiles = ((m + *tile_m - 1) / *tile_m) * ((n + *tile_n - 1) / *tile_n);
+    *split_tiles = sc.sp.split > 1 ? (int)(tiles - sc.sp.tiles_whole) : 0;
+    return hipSuccess;
 }
 
 hipError_t launch_gemm_scaled(int64_t m, int64_t n, int64_t k, const uint8_t* A, int fmt_a, const uint8_t* B,

@@ -38,6 +38,12 @@ hipError_t launch_gemm_mx(int64_t m, int64_t n, int64_t k, const uint8_t* A, int
                           int fmt_b, const uint8_t* ea, const uint8_t* eb, void* D, int out_f32,
                           hipStream_t stream);
 
+// the schedule a GEMM launch takes on a device with `cus` CUs (host only):
+// tile rows and columns, split count of the split tiles (1: none) and their
+// number; hipErrorInvalidValue beyond the 32-bit offset limits
+hipError_t schedule_gemm(int64_t m, int64_t n, int64_t k, int mx, int cus, int* tile_m, int* tile_n, int* split,
+                         int* split_tiles);
+
 // roof probes: matrix-core rate (blocks x 256 threads, iters rounds of 4
 // chains) and streaming bandwidth (bytes read, bytes / write_ratio written)
 hipError_t launch_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t stream);

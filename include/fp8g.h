@@ -18,6 +18,9 @@
  *   mxfp8_gemm_ex         chosen: E4M3 or E5M2
  *   concat_mla_k          MLA key rows: 128 "nope" + 64 "rope" elements of
  *                         1-byte (E4M3 / E5M2) or 2-byte type
+ *   fp8g_gemm_schedule    the tile and K split a GEMM launch takes (host only)
+ *   fp8g_roof_mfma,       roof probes: the matrix-core rate and the streaming
+ *   fp8g_roof_stream      bandwidth the part reaches at the moment
  *
  * Common conventions
  *   - Every array is dense and row-major; the caller owns all memory.  A is
@@ -375,6 +378,33 @@ int fp8g_roof_mfma(int64_t blocks, int64_t iters, float* sink, hipStream_t strea
 
 int fp8g_roof_stream(const void* src, int64_t bytes, void* dst, int write_ratio, int nontemporal_stores,
                      hipStream_t stream);
+
+/*
+ * fp8g_gemm_schedule -- the schedule fp8_gemm_scaled (mode 0; also the _ex and
+ * _noalloc forms) or mxfp8_gemm (mode 1; also mxfp8_gemm_ex) takes for an m x
+ * n x k problem on a device with `cus` compute units: the host-side choice the
+ * launch itself makes, exposed so that callers (and tests) can see it.
+ * Host only: no HIP call, no device needed.
+ *
+ * tile_m x tile_n  the output tile of a workgroup: 256 x 256; 128 x 128 when
+ *                  256 x 256 tiles would leave at least half of the CUs idle
+ *                  (mode 0 also when they spill just past one round); in mode
+ *                  0, 64 x 128 when 128 x 128 tiles would still leave half of
+ *                  the CUs idle and splitting them over K is not predicted
+ *                  faster.
+ * split            1, or the number of K ranges (2..4) each of the last
+ *                  round's 128 x 128 tiles is split into (mode 0, k a multiple
+ *                  of 128; such launches use the split workspace described at
+ *                  fp8_gemm_scaled, and under stream capture on a stream
+ *                  without one they run unsplit).
+ * split_tiles      the number of split tiles (0 when split == 1).
+ * The choice comes from cost models fitted to measurements on MI355X
+ * (256 CUs); other CU counts get the same rules.  m, n, k >= 0 and cus >= 1,
+ * else ERR_SHAPE; mode not 0 or 1: ERR_DTYPE; a NULL output: ERR_NULL; sizes
+ * beyond the GEMMs' limits: ERR_UNSUPPORTED.
+ */
+int fp8g_gemm_schedule(int64_t m, int64_t n, int64_t k, int mode, int cus, int* tile_m, int* tile_n, int* split,
+                       int* split_tiles);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fp8g_status_string(int status);

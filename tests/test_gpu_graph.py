@@ -110,6 +110,7 @@ def test_graph_split_k_on_a_stream_with_workspace(gpu_lib):
     bit, with eager split launches on another stream in between."""
     import torch
     (M, N, K), _, (A, B, sa, sb) = _split_case()
+    assert gpu_lib.fp8g_gemm_schedule(M, N, K)["split"] > 1
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         D = gpu_lib.fp8_gemm_scaled(M, N, K, A, B, sa, sb)
