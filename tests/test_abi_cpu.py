@@ -293,6 +293,11 @@ SCHEDULES_256 = [
     ((1024, 1024, 8192, 0), (128, 128, 4, 64)),     # long K: the split beats 64x128 tiles
     ((1024, 1024, 4096, 0), (64, 128, 1, 0)),       # K = 4096: 64x128 tiles beat the split
     ((2048, 1024, 8192, 0), (64, 128, 1, 0)),
+    ((1024, 512, 4096, 0), (64, 128, 1, 0)),
+    ((512, 1024, 8192, 0), (128, 128, 4, 32)),
+    ((2048, 512, 8192, 0), (128, 128, 4, 64)),
+    ((1000, 1001, 8192, 0), (128, 128, 4, 64)),
+    ((1000, 1024, 8192, 0), (128, 128, 4, 64)),
     ((4352, 4096, 8192, 0), (128, 128, 4, 64)),     # 272 tiles of 256 spill: 1088 of 128, last 64 split
     ((4352, 4096, 272, 0), (128, 128, 1, 0)),       # the same with a K tail: no split
     ((4352, 4096, 640, 1), (256, 256, 1, 0)),       # mode (b) keeps 256x256 tiles past one round
