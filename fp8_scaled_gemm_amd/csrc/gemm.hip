@@ -25,7 +25,9 @@
 // CUs more than pay for.  In mode (a), problems whose 128x128 tiles would
 // still fill at most half of the CUs (2048 x 1024: 128 tiles for 256 CUs) use
 // 64x128 tiles (waves of 32x64 = 1x2 blocks), unless splitting the 128x128
-// tiles over K is predicted faster.
+// tiles over K is predicted faster.  In mode (b), 256x128 tiles (waves of
+// 128x64 = 4x2 blocks) replace 256x256 ones where those leave a last round
+// of workgroups partly empty.
 //
 // K is walked in 64-byte steps, one V_MFMA_SCALE_F32_32X32X64_F8F6F4 per block
 // per step; mode (a) passes the neutral scale code 127 (2^0) and applies sa,
@@ -102,13 +104,15 @@ constexpr int GROUP_M = 8;
 // Tile geometry: a BM x BN output tile per workgroup (BM rows of A, BN rows of
 // B), 4 waves in 2x2, each wave WTM x WTN = NBM x NBN blocks of 32x32.  TILE
 // names the shape: 256 (256x256), 128 (128x128, for problems with few
-// tiles) or 64 (64x128, mode (a), for problems whose 128x128 tiles would
-// leave at least half of the CUs idle).
+// tiles), TILE_64x128 (mode (a), for problems whose 128x128 tiles would leave
+// at least half of the CUs idle) or TILE_256x128 (mode (b), for problems
+// whose 256x256 tiles leave a last round partly empty).
+constexpr int TILE_64x128 = 64128, TILE_256x128 = 256128;
 template <int TILE>
 struct Geo {
-    static constexpr int BM = TILE, BN = TILE == 64 ? 128 : TILE;
+    static constexpr int BM = TILE > 1000 ? TILE / 1000 : TILE, BN = TILE > 1000 ? TILE % 1000 : TILE;
     static constexpr int WTM = BM / 2, WTN = BN / 2;           // wave tile
-    static constexpr int NBM = WTM / 32, NBN = WTN / 32;       // blocks per wave tile: 4x4, 2x2 or 1x2
+    static constexpr int NBM = WTM / 32, NBN = WTN / 32;       // blocks per wave tile: 4x4, 2x2, 1x2 or 4x2
     // one operand of one stage (an "item"), and its loads per wave (1 KB per
     // wave instruction, 4 waves)
     static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
@@ -123,37 +127,47 @@ struct Geo {
 // (8 slots ran 5% slower there).  64x128 tiles (A items of 8 KB in slots of
 // 16 KB): 6 slots, loads 5 items ahead (at 2048x1024x4096: 13.0 us, against
 // 16.8 us with 5 slots, 15.0 us with 8 and 16.4 us with 10 slots of 24 KB
-// pairs).
+// pairs).  256x128 tiles (mode (b)): 3 pairs of a 32 KB A slot and a 16 KB B
+// slot (6 slots, loads 5 items ahead) and 12 KB of scale groups; the
+// epilogue borrows the B slot that is free then.
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
     using G = Geo<TILE>;
-    static_assert(!MX || G::BM == G::BN, "mode (b): square tiles");
     static constexpr bool SCALES = MX && !KTAIL;
-    static constexpr int NSLOT = TILE == 256 ? (SCALES ? 4 : 5) : TILE == 64 ? 6 : (MX ? 5 : 8);
+    static constexpr int NSLOT =
+        TILE == 256 ? (SCALES ? 4 : 5) : (TILE == TILE_64x128 || TILE == TILE_256x128) ? 6 : (MX ? 5 : 8);
+    // slot k holds items of index k modulo NSLOT; with slots of two sizes
+    // (COMPACT: even slots A items, odd ones B items, NSLOT even) each pair is
+    // A_BYTES + B_BYTES, otherwise every slot has the larger item's size
+    static constexpr bool COMPACT = TILE == TILE_256x128;
+    static_assert(!COMPACT || NSLOT % 2 == 0, "ring");
     static constexpr int SLOT = G::B_BYTES > G::A_BYTES ? G::B_BYTES : G::A_BYTES;
-    static constexpr int LDS = NSLOT * SLOT;
+    static constexpr int LDS = COMPACT ? NSLOT / 2 * (G::A_BYTES + G::B_BYTES) : NSLOT * SLOT;
     static constexpr int LA = G::LA, LB = G::LB;   // load instructions per item and wave, A and B
     // 4 slots hold two stages: stage g+2 can be loaded only once stage g's
     // slots are free (its step 1), so both its items are issued in that step
     // (none in step 0) to give them the longest lead.  5 or more slots: one
     // item per step, NSLOT-1 items ahead.
     static constexpr bool PAIRED = NSLOT == 4;
-    // mode (b) scale groups after the ring: 2 buffers x 2 operands x TILE rows
-    // x 16 bytes (the scales of SC_GROUP stages)
+    // mode (b) scale groups after the ring: 2 buffers of BM rows of A and BN
+    // rows of B x 16 bytes (the scales of SC_GROUP stages)
     static constexpr int SC_GROUP = 4;
     static constexpr int SC_AREA = LDS;
-    static constexpr int SC_OPER = G::BM * 16;
-    static constexpr int SC_BYTES = SCALES ? 4 * SC_OPER : 0;
+    static constexpr int SC_A = G::BM * 16, SC_B = G::BN * 16;
+    static constexpr int SC_BYTES = SCALES ? 2 * (SC_A + SC_B) : 0;
     // epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
-    // +16 KB): with 5 slots of 32 KB the slot that is free during the epilogue
-    // is borrowed; otherwise (paired, or 16 KB slots) a region of its own
-    static constexpr bool OWN_STAGE = PAIRED || TILE != 256;
+    // +16 KB): with 5 slots of 32 KB, or the 16 KB B slots of 256x128 tiles
+    // (mode (b) only), the slot that is free during the epilogue is borrowed;
+    // otherwise (paired, or 16 KB slots) a region of its own
+    static_assert(TILE != TILE_256x128 || MX, "256x128 tiles: mode (b)");
+    static constexpr bool OWN_STAGE = PAIRED || (TILE != 256 && TILE != TILE_256x128);
     static constexpr int STAGE_AREA = LDS + SC_BYTES;
     static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0);
 };
 static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
                   Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024 && Ring<false, false, 128>::LDS_TOTAL <= 160 * 1024 &&
-                  Ring<false, false, 64>::LDS_TOTAL <= 160 * 1024,
+                  Ring<false, false, TILE_64x128>::LDS_TOTAL <= 160 * 1024 &&
+                  Ring<true, false, TILE_256x128>::LDS_TOTAL <= 160 * 1024,
               "LDS");
 
 // The share of n items that slot k of s slots takes: one per slot while they
@@ -318,6 +332,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     static_assert(!R::PAIRED || LA == LB, "paired ring: square tiles");
     // loads of n consecutive items that start with an A item
     auto loads_of = [](int n) constexpr { return (n + 1) / 2 * LA + n / 2 * LB; };
+    // LDS byte offset of ring slot k
+    auto slot_off = [&](int k) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (!R::COMPACT) return (uint32_t)(k * SLOT);
+        else return (uint32_t)((k >> 1) * (GEO::A_BYTES + GEO::B_BYTES) + (k & 1) * GEO::A_BYTES);
+    };
     // lane L of wave w, instruction p fills row 32p + 8w + L/8, slot L%8, which
     // holds logical chunk (L%8) ^ ((row >> 1) & 7) = (L%8) ^ ((4w + L/16) & 7)
     const uint32_t dma_chunk = (uint32_t)((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7));
@@ -339,7 +358,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // load q (0..LA-1 or 0..LB-1) of the cursor's item
     auto dma_item = [&](int q) __attribute__((always_inline)) {
         const int s_ld = (ii < 2 * NS) ? is : ins - 1;   // past the end: reload the last stage
-        const uint32_t sbuf = lds0 + (uint32_t)(islot * SLOT);
+        const uint32_t sbuf = lds0 + slot_off(islot);
         const uint32_t k0 = (uint32_t)((ikb + s_ld) * BK);
         uint32_t voff = dma_voff;
         if constexpr (KTAIL) {
@@ -353,14 +372,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // ---- mode (b) scale groups (whole scale dwords, K % 128 == 0).  Group gi
     // of a tile covers its stages 4gi .. 4gi+3: bytes 16gi .. 16gi+15 of every
     // scale row.  Stream group number u (tile j: u = j * ngt + gi) goes to
-    // buffer u & 1, operand o at SC_AREA + (2 (u & 1) + o) * TILE * 16: row r
-    // in the 16 bytes at 16 r, the dword of group stage t at position
+    // buffer u & 1 at SC_AREA + (u & 1) (SC_A + SC_B), A's rows first, then
+    // B's (sc_area): row r in the 16 bytes at 16 r, the dword of group stage t at position
     // (t + (r >> 3)) & 3 (rotated so that the 32 rows of one scale read fall in
     // distinct banks).  Load p of an operand fills rows 16p .. 16p+15, lane L
     // row 16p + L/4 at position L % 4: 16 bytes of a row in one or two lines,
     // where loading each stage's dword alone touches a line per row per stage.
-    // Wave w issues loads p = w, w+4, ... of both operands.
-    constexpr int SC_LOADS = R::SCALES ? 2 * (BM / 16) / 4 : 0;   // per wave and group: 8 or 4
+    // Wave w issues loads p = w, w+4, ... of both operands: SC_LA of A, then
+    // SC_LB of B.
+    constexpr int SC_LA = R::SCALES ? BM / 16 / 4 : 0, SC_LB = R::SCALES ? BN / 16 / 4 : 0;
+    constexpr int SC_LOADS = SC_LA + SC_LB;   // per wave and group: 8, 4 or 6
+    // LDS byte offset of buffer ub's scale rows of operand o
+    auto sc_area = [](int ub, int o) constexpr -> int {
+        if constexpr (R::SC_A == R::SC_B) return R::SC_AREA + 2 * ub * R::SC_A + o * R::SC_A;
+        else return R::SC_AREA + ub * (R::SC_A + R::SC_B) + o * R::SC_A;
+    };
     const int ngt = (nk + R::SC_GROUP - 1) / R::SC_GROUP;            // groups per tile
     const uint32_t sc_voff = (uint32_t)(16 * wave + (lane >> 2)) * (uint32_t)nblk +
                              4u * (((uint32_t)(lane & 3) - (uint32_t)(2 * wave + (lane >> 5))) & 3u);
@@ -374,11 +400,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // load q (0 .. SC_LOADS-1) of group gi (of the tile of rsEA, rsEB) into buffer ub
     auto sc_load = [&](int q, int gi, int ub) __attribute__((always_inline)) {
         if constexpr (R::SCALES) {
-            constexpr int PER_OP = SC_LOADS / 2;
-            const int o = q / PER_OP, p = wave + 4 * (q % PER_OP);
-            const uint32_t dst = lds0 + (uint32_t)(R::SC_AREA + (2 * ub + o) * R::SC_OPER + 256 * p);
-            dma4(uniform(dst), sc_voff, o ? rsEB : rsEA,
-                 uniform((uint32_t)(16 * gi) + (uint32_t)(64 * (q % PER_OP)) * (uint32_t)nblk));
+            if constexpr (R::SC_A == R::SC_B) {
+                constexpr int PER_OP = SC_LOADS / 2;
+                const int o = q / PER_OP, p = wave + 4 * (q % PER_OP);
+                const uint32_t dst = lds0 + (uint32_t)(R::SC_AREA + (2 * ub + o) * R::SC_A + 256 * p);
+                dma4(uniform(dst), sc_voff, o ? rsEB : rsEA,
+                     uniform((uint32_t)(16 * gi) + (uint32_t)(64 * (q % PER_OP)) * (uint32_t)nblk));
+            } else {
+                const int o = q < SC_LA ? 0 : 1, idx = o ? q - SC_LA : q, p = wave + 4 * idx;
+                const uint32_t dst = lds0 + (uint32_t)(sc_area(ub, o) + 256 * p);
+                dma4(uniform(dst), sc_voff, o ? rsEB : rsEA,
+                     uniform((uint32_t)(16 * gi) + (uint32_t)(64 * idx) * (uint32_t)nblk));
+            }
         }
     };
     auto advance = [&]() __attribute__((always_inline)) {
@@ -429,14 +462,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                 const int l32s = ln & 31;
                 const uint32_t sh = (uint32_t)(8 * (ln >> 5));
                 const int ub = (j * ngt + s / R::SC_GROUP) & 1;
-                const uint8_t* sca = smem + R::SC_AREA + 2 * ub * R::SC_OPER;
-                const uint8_t* scb = sca + R::SC_OPER;
+                const uint8_t* sca;
+                const uint8_t* scb;
+                if constexpr (R::SC_A == R::SC_B) {
+                    sca = smem + R::SC_AREA + 2 * ub * R::SC_A;
+                    scb = sca + R::SC_A;
+                } else {
+                    sca = smem + sc_area(ub, 0);
+                    scb = smem + sc_area(ub, 1);
+                }
                 // row wm*WTM + 32i + l32: (row >> 3) & 3 == (l32 >> 3) & 3
                 const uint32_t pos = (((uint32_t)(s & 3) + (uint32_t)(l32s >> 3)) & 3u) * 4u;
 #pragma unroll
-                for (int i = 0; i < NBM; ++i) {
-                    xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WTM + i * 32 + l32s) * 16 + pos) >> sh;
-                    xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WTN + i * 32 + l32s) * 16 + pos) >> sh;
+                for (int i = 0; i < NBX; ++i) {
+                    if (i < NBM)
+                        xa[i] = *reinterpret_cast<const uint32_t*>(sca + (wm * WTM + i * 32 + l32s) * 16 + pos) >> sh;
+                    if (i < NBN)
+                        xb[i] = *reinterpret_cast<const uint32_t*>(scb + (wn * WTN + i * 32 + l32s) * 16 + pos) >> sh;
                 }
             } else {
                 const TileCoord tc = tile_of(j);
@@ -447,13 +489,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
                 const bool in = kb < nblk;
                 const uint32_t kc = (uint32_t)min(kb, nblk - 1);
 #pragma unroll
-                for (int i = 0; i < NBM; ++i) {
-                    const uint32_t va = __builtin_amdgcn_raw_buffer_load_b8(
-                        pa, (uint32_t)(wm * WTM + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
-                    const uint32_t vb = __builtin_amdgcn_raw_buffer_load_b8(
-                        pb, (uint32_t)(wn * WTN + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
-                    xa[i] = in ? va : 127u;
-                    xb[i] = in ? vb : 127u;
+                for (int i = 0; i < NBX; ++i) {
+                    if (i < NBM) {
+                        const uint32_t va = __builtin_amdgcn_raw_buffer_load_b8(
+                            pa, (uint32_t)(wm * WTM + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
+                        xa[i] = in ? va : 127u;
+                    }
+                    if (i < NBN) {
+                        const uint32_t vb = __builtin_amdgcn_raw_buffer_load_b8(
+                            pb, (uint32_t)(wn * WTN + i * 32 + l32) * (uint32_t)nblk + kc, 0, 0);
+                        xb[i] = in ? vb : 127u;
+                    }
                 }
             }
         }
@@ -861,7 +907,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 #pragma unroll
     for (int i = 0; i < NBX; ++i) {
         if (i < NBM) fa0[i] = frag(0, frag_a, 0, i);
-        if (i < NBN) fb0[i] = frag(SLOT, frag_b, 0, i);
+        if (i < NBN) fb0[i] = frag(slot_off(1), frag_b, 0, i);
     }
     read_scales(0, 0, 0, xa, xb);
     int rslot = 0;   // LDS slot of the current stage's A item (its B item is the next slot)
@@ -937,13 +983,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             // epilogue (before this step's item loads, so that waiting for all
             // but those leaves the scales landed)
             if constexpr (!MX && LAST) {
-                tile_scales_to_lds(j, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, 1) * SLOT));
+                tile_scales_to_lds(j, R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : slot_off(slot_add(rslot, 1)));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         const int sn = h ? s + 1 : s, hn = h ^ 1;
         const int na_slot = h ? slot_add(rslot, 2) : rslot;   // slots of the items read next
-        const uint32_t sa_off = (uint32_t)(na_slot * SLOT), sb_off = (uint32_t)(slot_add(na_slot, 1) * SLOT);
+        const uint32_t sa_off = slot_off(na_slot), sb_off = slot_off(slot_add(na_slot, 1));
         uint32_t nxa[NBM], nxb[NBN];
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
@@ -1022,7 +1068,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         kstep(acc, j, nsj - 1, Step1{}, Last{}, fa1, fb1, fa0, fb0);
         // the slot of the last stage's B item is free until the next K step
         // loads into it (every wave finished reading it before the last barrier)
-        const uint32_t stage_off = R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : (uint32_t)(slot_add(rslot, NSLOT - 1) * SLOT);
+        const uint32_t stage_off = R::OWN_STAGE ? (uint32_t)R::STAGE_AREA : slot_off(slot_add(rslot, NSLOT - 1));
         if constexpr (SPLIT) {
             // the split item is the workgroup's last: the one that does not add
             // up the tile has no epilogue and nothing after it
@@ -1048,8 +1094,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         // that exists (the K-tail path reads them from global memory).
 #pragma unroll
         for (int i = 0; i < NBX; ++i) {
-            if (i < NBM) fa0[i] = frag((uint32_t)(rslot * SLOT), frag_a, 0, i);
-            if (i < NBN) fb0[i] = frag((uint32_t)(slot_add(rslot, 1) * SLOT), frag_b, 0, i);
+            if (i < NBM) fa0[i] = frag(slot_off(rslot), frag_a, 0, i);
+            if (i < NBN) fb0[i] = frag(slot_off(slot_add(rslot, 1)), frag_b, 0, i);
         }
         if (j + 1 < my_tiles) read_scales(j + 1, 0, 0, xa, xb);
     }
@@ -1209,10 +1255,20 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
 //   the CUs idle and splitting them over K is not predicted faster
 //   (prefer_tile64): twice the workgroups, each with half the matrix-core
 //   work per stage.
+//   256x128 tiles (mode (b)) in place of 256x256 ones when they need at most
+//   1.5 times the rounds: a round of 256x128 tiles costs 0.57-0.66 of a round
+//   of 256x256 tiles (measured at 132 to 896 tiles of 256x256), so they pay
+//   where 256x256 tiles leave a last round partly empty and lose where that
+//   round is nearly full.  Measured (256x256 / 256x128 tiles):
+//   2600x2900x1024 22.7 / 17.9 us (132 tiles of 256x256; 1 round against 1),
+//   4352x4096x640 25.4 / 23.0 us (272; 2 rounds against 3), 4096x6144x2048
+//   55.9 / 55.2 us (384; 2 against 3); 3072x4096x1024 18.5 / 21.4 us (192;
+//   1 against 2), 4096x8192x2048 66.4 / 76.0 us (512; 2 against 4),
+//   4096x14336x4096 197.9 / 225.0 us (896; 4 against 7).
 //   Only 128x128 tiles split: the 256x256 split kernel would spill around its
 //   last step.
 struct Schedule {
-    int tile;       // 256, 128 or 64 (64x128)
+    int tile;       // 256, 128, TILE_64x128 or TILE_256x128
     SplitPlan sp;   // split == 1: no split
 };
 static Schedule gemm_schedule(int64_t m, int64_t n, int64_t k, bool mx, int cus) {
@@ -1224,11 +1280,16 @@ static Schedule gemm_schedule(int64_t m, int64_t n, int64_t k, bool mx, int cus)
         if (!mx) {
             if (!spill && 2 * tiles128 <= cus && prefer_tile64(tiles128, cus, k / BK, tail)) {
                 const int64_t tiles64 = ((m + 63) / 64) * ((n + 127) / 128);
-                return {64, {(int)tiles64, 1}};
+                return {TILE_64x128, {(int)tiles64, 1}};
             }
             if (!tail) return {128, split_plan(tiles128, cus, k / BK)};
         }
         return {128, {(int)tiles128, 1}};
+    }
+    if (mx) {
+        const int64_t tiles_h = ((m + 255) / 256) * ((n + 127) / 128);   // 256x128 tiles
+        const int64_t rounds = (tiles256 + cus - 1) / cus, rounds_h = (tiles_h + cus - 1) / cus;
+        if (2 * rounds_h <= 3 * rounds) return {TILE_256x128, {(int)tiles_h, 1}};
     }
     return {256, {(int)tiles256, 1}};
 }
@@ -1279,9 +1340,13 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
     if (e != hipSuccess) return e;
     const Schedule sc = gemm_schedule(m, n, k, MX, cus);
     if constexpr (!MX) {
-        if (sc.tile == 64)
-            return launch_tiled<MX, FA, FB, 64>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws,
-                                                stream);
+        if (sc.tile == TILE_64x128)
+            return launch_tiled<MX, FA, FB, TILE_64x128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp,
+                                                         fixed_ws, stream);
+    } else {
+        if (sc.tile == TILE_256x128)
+            return launch_tiled<MX, FA, FB, TILE_256x128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp,
+                                                          fixed_ws, stream);
     }
     if (sc.tile == 128)
         return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws,
@@ -1345,8 +1410,8 @@ hipError_t schedule_gemm(int64_t m, int64_t n, int64_t k, int mx, int cus, int* 
                          int* split_tiles) {
     if (!fits(m, n, k)) return hipErrorInvalidValue;
     const Schedule sc = gemm_schedule(m, n, k, mx != 0, cus);
-    *tile_m = sc.tile;
-    *tile_n = sc.tile == 64 ? 128 : sc.tile;
+    *tile_m = sc.tile > 1000 ? sc.tile / 1000 : sc.tile;
+    *tile_n = sc.tile > 1000 ? sc.tile % 1000 : sc.tile;
     *split = sc.sp.split;
     const int64_t tiles = ((m + *tile_m - 1) / *tile_m) * ((n + *tile_n - 1) / *tile_n);
     *split_tiles = sc.sp.split > 1 ? (int)(tiles - sc.sp.tiles_whole) : 0;

@@ -300,7 +300,11 @@ SCHEDULES_256 = [
     ((1000, 1024, 8192, 0), (128, 128, 4, 64)),
     ((4352, 4096, 8192, 0), (128, 128, 4, 64)),     # 272 tiles of 256 spill: 1088 of 128, last 64 split
     ((4352, 4096, 272, 0), (128, 128, 1, 0)),       # the same with a K tail: no split
-    ((4352, 4096, 640, 1), (256, 256, 1, 0)),       # mode (b) keeps 256x256 tiles past one round
+    ((4352, 4096, 640, 1), (256, 128, 1, 0)),       # mode (b): 272 tiles of 256x256 (2 rounds), 544 of 256x128 (3)
+    ((2600, 2900, 1024, 1), (256, 128, 1, 0)),      # 132 of 256x256, 253 of 256x128: one round either way
+    ((2561, 3000, 1056, 1), (256, 256, 1, 0)),      # 264 of 256x128: twice the rounds
+    ((3072, 4096, 1024, 1), (256, 256, 1, 0)),      # 192 of 256x256 (1 round) against 384 (2)
+    ((4096, 8192, 2048, 1), (256, 256, 1, 0)),      # 2 rounds against 4
     ((1000, 1001, 272, 0), (64, 128, 1, 0)),        # K tail
     ((300, 512, 0, 0), (64, 128, 1, 0)),            # k = 0
 ]

@@ -160,7 +160,7 @@ def test_mode_a_k_zero(gpu_lib, M, N, out):
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-@pytest.mark.parametrize("M,N", [(70, 90), (2600, 3072)])
+@pytest.mark.parametrize("M,N", [(70, 90), (2600, 2900), (2600, 3072), (4096, 8192)])
 def test_mode_b_k_zero(gpu_lib, M, N, out):
     import torch
     A = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
@@ -296,8 +296,14 @@ def mx_scales(seed, R, nb, stream):
     return (synth.u8_codes(seed, stream, (R, nb), exclude_nan=False) % 41 + 107).astype(np.uint8)
 
 
+# On a 256-CU part: up to 512 x 512 the 128x128 tiles; 2600 x 2900 (132
+# tiles of 256x256, 253 of 256x128: one round either way) the 256x128 tiles;
+# 2561 x 3000 (264 of 256x128: two rounds) and 2304 x 4000 (144 tiles of
+# 256x256, 288 of 256x128) the 256x256 tiles.  Ragged m and n throughout,
+# with and without a K tail.
 SHAPES_B = [(32, 32, 32), (64, 96, 96), (256, 256, 256), (257, 300, 4128), (512, 512, 1024), (5, 700, 160),
-            (300, 7, 64), (2561, 3000, 1056), (2600, 2900, 1024)]
+            (300, 7, 64), (2561, 3000, 1056), (2600, 2900, 1024), (2600, 2900, 1056), (2304, 4000, 1024),
+            (2304, 4000, 1056)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -341,14 +347,15 @@ def test_mode_b_scale_association(gpu_lib):
             assert np.array_equal(D, want), (j, t)
 
 
-def test_mode_b_scale_association_256_tiles(gpu_lib):
-    """The same one-product-per-output association check at 4352 x 4096 x 256,
-    which runs on 256x256 tiles (272 of them for 256 workgroups: some
-    workgroups take a second tile) through the paired ring whose steps pick
-    their block's scale byte in the matrix-core instruction; every element of
-    D is compared."""
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 256), (4096, 8192, 256)])
+def test_mode_b_scale_association_256_tiles(gpu_lib, M, N, K):
+    """The same one-product-per-output association check on 256-row tiles,
+    where the matrix-core steps pick their block's scale byte in the
+    instruction: 4352 x 4096 runs on 544 tiles of 256x128 (a 6-slot ring,
+    scale groups of 256 A rows and 128 B rows), 4096 x 8192 on 512 tiles of
+    256x256 (the paired ring); both give some workgroups more than one tile.
+    Every element of D is compared."""
     import torch
-    M, N, K = 4352, 4096, 256
     base_a = np.array([0x38, 0x7E, 0x81, 0xB9], np.uint8)
     base_b = np.array([0x40, 0xB9, 0x01, 0x7E], np.uint8)
     am, bn = base_a[np.arange(M) % 4], base_b[np.arange(N) % 4]
@@ -371,11 +378,14 @@ def test_mode_b_scale_association_256_tiles(gpu_lib):
 
 # Neutral block scales (code 127) make mode (b) compute mode (a) with unit
 # scales through the same matrix-core instruction, so the two must agree bit
-# for bit.  On 4864 x 4096 (304 tiles of 256, two per workgroup for some) the
-# fp32 outputs come from different epilogues -- staged through LDS in mode (a),
-# from registers in mode (b) -- which this compares exactly.
+# for bit, whatever tiles each takes: each output sums its K steps in the same
+# order.  On 4864 x 4096 (304 tiles of 256x256 in mode (a), 608 of 256x128 in
+# mode (b)) and 4096 x 8192 (512 tiles of 256x256 in both) workgroups run
+# second tiles, and the fp32 outputs come from different epilogues -- staged
+# through LDS in mode (a), from registers in mode (b) -- which this compares
+# exactly.
 @pytest.mark.parametrize("M,N,K,out", [(300, 260, 1024, "f32"), (4864, 4096, 1024, "f32"),
-                                       (4864, 4096, 1024, "bf16")])
+                                       (4864, 4096, 1024, "bf16"), (4096, 8192, 1024, "f32")])
 def test_mode_b_neutral_scales_equal_mode_a(gpu_lib, M, N, K, out):
     A, B = codes(3, (M, K)), codes(3, (N, K), 2)
     ea = np.full((M, K // 32), 127, np.uint8)
@@ -418,11 +428,11 @@ def test_mode_b_mx_workload(gpu_lib):
 # staged together, so the last group of a tile is partial unless the stages
 # per tile (K / 128) are a multiple of 4, and with more tiles than workgroups
 # a workgroup's next tile's first group is loaded during its current tile.
-# 4352 x 4096: 272 tiles of 256 for 256 workgroups; 2048 x 4096: 128 tiles of
-# 256, so 512 tiles of 128 (two per workgroup).  Rows and columns sampled at
-# a stride cover every tile.
+# 4352 x 4096: 544 tiles of 256x128 for 256 workgroups; 4096 x 8192: 512
+# tiles of 256x256; 2048 x 4096: 128 tiles of 256, so 512 tiles of 128 (two
+# per workgroup).  Rows and columns sampled at a stride cover every tile.
 SHAPES_B_GROUPS = [(4352, 4096, 128), (4352, 4096, 384), (4352, 4096, 640), (4352, 4096, 1664),
-                   (2048, 4096, 640), (2048, 4096, 896)]
+                   (4096, 8192, 384), (4096, 8192, 640), (2048, 4096, 640), (2048, 4096, 896)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES_B_GROUPS)

@@ -143,9 +143,11 @@ def test_ex_dtype_checks(gpu_lib):
         gpu_lib.fp8_gemm_scaled_ex(4, 4, 64, A.view(torch.uint8), 2, B, E5M2, s, s)
 
 
-# K / 128 = 3 and 5: the last group of 4 stages' block scales is partial
+# K / 128 = 3 and 5: the last group of 4 stages' block scales is partial.  On
+# a 256-CU part 2600 x 2900 runs on 256x128 tiles and 2304 x 4000 (K tail) on
+# 256x256 tiles; the rest on 128x128 tiles.
 SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160), (2600, 2900, 1024),
-            (300, 260, 384), (200, 300, 640)]
+            (2304, 4000, 160), (300, 260, 384), (200, 300, 640)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -186,12 +188,12 @@ def test_ex_mode_b_scale_association_e5m2(gpu_lib):
         assert np.array_equal(D, want), j
 
 
-def test_ex_mode_b_scale_groups_e5m2(gpu_lib):
-    """E5M2 x E5M2 MX at 4352 x 4096 x 640: 272 tiles of 256 for 256
-    workgroups, 5 stages per tile (a partial last group of 4 stages' block
-    scales, and groups loaded for a workgroup's next tile); rows and columns
-    sampled at a stride cover every tile."""
-    M, N, K = 4352, 4096, 640
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 640), (4096, 8192, 640)])
+def test_ex_mode_b_scale_groups_e5m2(gpu_lib, M, N, K):
+    """E5M2 x E5M2 MX with 5 stages per tile (a partial last group of 4
+    stages' block scales, and groups loaded for a workgroup's next tile), on
+    544 tiles of 256x128 (4352 x 4096) and 512 of 256x256 (4096 x 8192) for
+    256 workgroups; rows and columns sampled at a stride cover every tile."""
     seed = 99
     A, B = finite_codes(seed, (M, K), E5M2), finite_codes(seed, (N, K), E5M2, 2)
     ea = (synth.u8_codes(seed, 7, (M, K // 32)) % 41 + 107).astype(np.uint8)
