@@ -181,12 +181,17 @@ TRAFFIC_FILES = {"ffn_up": "profiles/gemm_fp8_ffn_up_8192x22016x8192_hbm_traffic
                  "quantize": "profiles/quantize_rows_f32_e4m3_8192x8192_hbm_traffic.txt"}
 
 
-def source_digest(name="gemm.hip"):
-    """sha256 of a kernel source file: counters taken on another version of it
-    do not describe the kernel being timed."""
+def code_digest(name="gemm.hip"):
+    """sha256 of a kernel source file's code, without its comments and
+    whitespace: counters taken on another version of the code do not describe
+    the kernel being timed, while an edit of a comment changes nothing."""
     import hashlib
-    with open(os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    with open(os.path.join(ROOT, "fp8_scaled_gemm_amd", "csrc", name)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+    text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()
 
 
 def read_traffic(path, source="gemm.hip"):
@@ -200,7 +205,7 @@ def read_traffic(path, source="gemm.hip"):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_digest(source):
+    if kv.get("code_sha256") != code_digest(source):
         log("traffic summary %s was taken on another kernel source: traffic = null" % path)
         return None
     try:

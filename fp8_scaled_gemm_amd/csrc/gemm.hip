@@ -914,20 +914,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
 
     // ---- one K step: step h of stage s of stream tile j (fragments and scales
     // in registers).
-    //   the 4 matrix-core steps of row block 0;
+    //   the NBM matrix-core steps of row block 0 (4 for 256-row tiles);
     //   h == 1 only: wait until the next stage's items landed (items past them
     //   may be in flight) and sync: they landed for every wave, and every wave's
     //   reads of this stage's items (done during step 0) are finished (the
     //   barrier waits for outstanding LDS reads), so their slots may be refilled;
-    //   12 slots, each one matrix-core step plus one load of the item NSLOT-1
-    //   ahead (into the slot of the item just before this step's) and two
-    //   16-byte LDS reads of the next step's fragments into the other register
-    //   set.  Spreading the loads keeps the address unit from blocking the
+    //   the remaining (NBN-1)·NBM matrix-core steps ("slots": 12 for 256x256
+    //   tiles), each with its share of the loads of the item NSLOT-1 ahead
+    //   (into the slot of the item just before this step's) and of the next
+    //   step's fragment reads (two 16-byte LDS reads each) into the other
+    //   register set.  Spreading the loads keeps the address unit from blocking the
     //   matrix-core steps behind a burst of loads from all four waves.
     //   LAST (the tile's last step): no reads of the next step's fragments (they
     //   are read after the epilogue, which then has their registers to itself).
-    // matrix-core steps after row block 0 (12, 2 for 128x128 and 1 for 64x128 tiles); the
-    // step's loads and the next step's NBM + NBN fragment reads are spread over them.
+    // matrix-core steps after row block 0: 12 for 256x256 tiles, 4 for
+    // 256x128, 2 for 128x128 and 1 for 64x128; the step's loads and the next
+    // step's NBM + NBN fragment reads are spread over them.
     // Mode (b) scales from LDS (once per stage, in its step 1, for the next
     // stage) are read first, in slot 0: LDS reads complete in order, so scales
     // read after the fragments would hold the next step's first matrix-core
@@ -938,8 +940,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // group (the tile's next, or the next tile's first) into the other buffer,
     // whose group was last read in step 0 of the stage before, ahead of the
     // barrier of that stage's step 1.  The paired ring spreads the loads over
-    // this step, which loads no items; with 5 slots they go first, before the
-    // item loads, which the next wait may leave in flight.  Either way they
+    // this step, which loads no items; with 5 or more slots they go first,
+    // before the item loads, which the next wait may leave in flight.  Either way they
     // have landed at that wait, the earliest point the group is read.
     constexpr int SLOTS = (NBN - 1) * NBM;
     constexpr int NREAD = NBM + NBN;
