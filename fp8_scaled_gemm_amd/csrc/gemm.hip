@@ -25,7 +25,7 @@
 // CUs more than pay for.  In mode (a), problems whose 128x128 tiles would
 // still fill at most half of the CUs (2048 x 1024: 128 tiles for 256 CUs) use
 // 64x128 tiles (waves of 32x64 = 1x2 blocks), unless splitting the 128x128
-// tiles over K is predicted faster.  In mode (b), 256x128 tiles (waves of
+// tiles over K is predicted faster.  In both modes, 256x128 tiles (waves of
 // 128x64 = 4x2 blocks) replace 256x256 ones where those leave a last round
 // of workgroups partly empty.
 //
@@ -105,8 +105,8 @@ constexpr int GROUP_M = 8;
 // B), 4 waves in 2x2, each wave WTM x WTN = NBM x NBN blocks of 32x32.  TILE
 // names the shape: 256 (256x256), 128 (128x128, for problems with few
 // tiles), TILE_64x128 (mode (a), for problems whose 128x128 tiles would leave
-// at least half of the CUs idle) or TILE_256x128 (mode (b), for problems
-// whose 256x256 tiles leave a last round partly empty).
+// at least half of the CUs idle) or TILE_256x128 (for problems whose 256x256
+// tiles leave a last round partly empty).
 constexpr int TILE_64x128 = 64128, TILE_256x128 = 256128;
 template <int TILE>
 struct Geo {
@@ -127,8 +127,8 @@ struct Geo {
 // (8 slots ran 5% slower there).  64x128 tiles (A items of 8 KB in slots of
 // 16 KB): 6 slots, loads 5 items ahead (at 2048x1024x4096: 13.0 us, against
 // 16.8 us with 5 slots, 15.0 us with 8 and 16.4 us with 10 slots of 24 KB
-// pairs).  256x128 tiles (mode (b)): 3 pairs of a 32 KB A slot and a 16 KB B
-// slot (6 slots, loads 5 items ahead) and 12 KB of scale groups; the
+// pairs).  256x128 tiles: 3 pairs of a 32 KB A slot and a 16 KB B slot (6
+// slots, loads 5 items ahead), in mode (b) and 12 KB of scale groups; the
 // epilogue borrows the B slot that is free then.
 template <bool MX, bool KTAIL, int TILE>
 struct Ring {
@@ -156,18 +156,23 @@ struct Ring {
     static constexpr int SC_A = G::BM * 16, SC_B = G::BN * 16;
     static constexpr int SC_BYTES = SCALES ? 2 * (SC_A + SC_B) : 0;
     // epilogue staging (16 KB; in mode (a) also the tile's sa, sb at
-    // +16 KB): with 5 slots of 32 KB, or the 16 KB B slots of 256x128 tiles
-    // (mode (b) only), the slot that is free during the epilogue is borrowed;
-    // otherwise (paired, or 16 KB slots) a region of its own
-    static_assert(TILE != TILE_256x128 || MX, "256x128 tiles: mode (b)");
+    // +16 KB): with 5 slots of 32 KB, or the 16 KB B slots of 256x128 tiles,
+    // the slot that is free during the epilogue is borrowed; otherwise
+    // (paired, or 16 KB slots) a region of its own.  Mode (a) on 256x128
+    // tiles keeps the tile's sa, sb in 2 KB of their own after the ring
+    // (TS_SEPARATE, at TS_AREA), since the borrowed B slot holds only the
+    // 16 KB of staging.
     static constexpr bool OWN_STAGE = PAIRED || (TILE != 256 && TILE != TILE_256x128);
     static constexpr int STAGE_AREA = LDS + SC_BYTES;
-    static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0);
+    static constexpr bool TS_SEPARATE = !MX && TILE == TILE_256x128;
+    static constexpr int TS_AREA = STAGE_AREA;
+    static constexpr int LDS_TOTAL = STAGE_AREA + (OWN_STAGE ? (MX ? 16 : 18) * 1024 : 0) + (TS_SEPARATE ? 2048 : 0);
 };
 static_assert(Ring<false, false, 256>::LDS_TOTAL <= 160 * 1024 && Ring<true, false, 256>::LDS_TOTAL <= 160 * 1024 &&
                   Ring<true, false, 128>::LDS_TOTAL <= 160 * 1024 && Ring<false, false, 128>::LDS_TOTAL <= 160 * 1024 &&
                   Ring<false, false, TILE_64x128>::LDS_TOTAL <= 160 * 1024 &&
-                  Ring<true, false, TILE_256x128>::LDS_TOTAL <= 160 * 1024,
+                  Ring<true, false, TILE_256x128>::LDS_TOTAL <= 160 * 1024 &&
+                  Ring<false, false, TILE_256x128>::LDS_TOTAL <= 160 * 1024,
               "LDS");
 
 // The share of n items that slot k of s slots takes: one per slot while they
@@ -531,6 +536,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
     // also wait for the next tile's operand loads in flight.
     constexpr int ESZ = OUT_F32 ? 4 : 2;
     constexpr uint32_t SC_OFF = 16384;   // the tile's sa at stage_off + 16 KB, sb at + 17 KB
+    // LDS offset of the tile's sa (sb 1 KB after it) for the staging region at stage_off
+    auto ts_off = [&](uint32_t stage_off) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (R::TS_SEPARATE) return (uint32_t)R::TS_AREA;
+        else return stage_off + SC_OFF;
+    };
     auto epilogue = [&](int j, v16f (&acc)[NBN][NBM], uint32_t stage_off) __attribute__((always_inline)) {
         const TileCoord tc = tile_of(j);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
@@ -540,8 +550,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         constexpr uint32_t OOB = 0x80000000u;   // beyond any panel (panels are < 2^31 bytes)
         const int lane_u = fresh_lane();
         const int l32 = lane_u & 31, lhi = lane_u >> 5;
-        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
-        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
+        const float* lsa = reinterpret_cast<const float*>(smem + ts_off(stage_off));
+        const float* lsb = reinterpret_cast<const float*>(smem + ts_off(stage_off) + 1024);
         float smv[NBM], snv[NBN][4][4];
 #pragma unroll
         for (int jb = 0; jb < NBM; ++jb) {
@@ -624,9 +634,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
             const TileCoord tc = tile_of(j);
             const int m0 = tc.tm * BM, n0 = tc.tn * BN;
             const uint32_t v = (uint32_t)(64 * wave + fresh_lane()) * 4u;   // lane L of wave w: element 64w + L
-            dma4(uniform(lds0 + stage_off + SC_OFF + (uint32_t)(wave * 256)), v,
+            dma4(uniform(lds0 + ts_off(stage_off) + (uint32_t)(wave * 256)), v,
                  panel(sa + m0, (uint32_t)min(BM, M - m0) * 4u), 0u);
-            dma4(uniform(lds0 + stage_off + SC_OFF + 1024u + (uint32_t)(wave * 256)), v,
+            dma4(uniform(lds0 + ts_off(stage_off) + 1024u + (uint32_t)(wave * 256)), v,
                  panel(sb + n0, (uint32_t)min(BN, N - n0) * 4u), 0u);
         }
     };
@@ -640,8 +650,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int lane_e = fresh_lane();
         const int l32e = lane_e & 31, lhie = lane_e >> 5;
         uint8_t* st = smem + stage_off + wave * 4096;
-        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
-        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
+        const float* lsa = reinterpret_cast<const float*>(smem + ts_off(stage_off));
+        const float* lsb = reinterpret_cast<const float*>(smem + ts_off(stage_off) + 1024);
         const uint32_t wkey = (uint32_t)((l32e >> 1) & 7), whalf = (uint32_t)(lhie ^ (l32e >> 4));
         // rows past M need no check: the descriptor covers exactly the tile's rows
         // of D, and offsets past it are dropped
@@ -717,8 +727,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_fp8_kernel(
         const int lane_e = fresh_lane();
         const int l32e = lane_e & 31, lhie = lane_e >> 5;
         uint8_t* st = smem + stage_off + wave * 4096;
-        const float* lsa = reinterpret_cast<const float*>(smem + stage_off + SC_OFF);
-        const float* lsb = reinterpret_cast<const float*>(smem + stage_off + SC_OFF + 1024);
+        const float* lsa = reinterpret_cast<const float*>(smem + ts_off(stage_off));
+        const float* lsb = reinterpret_cast<const float*>(smem + ts_off(stage_off) + 1024);
         const uint32_t wkey = (uint32_t)((l32e >> 1) & 7);
         // rows past M need no check: the descriptor covers exactly the tile's rows
         // of D, and offsets past it are dropped
@@ -1257,16 +1267,23 @@ static hipError_t launch_one(int64_t m, int64_t n, int64_t k, const uint8_t* A, 
 //   the CUs idle and splitting them over K is not predicted faster
 //   (prefer_tile64): twice the workgroups, each with half the matrix-core
 //   work per stage.
-//   256x128 tiles (mode (b)) in place of 256x256 ones when they need at most
-//   1.5 times the rounds: a round of 256x128 tiles costs 0.57-0.66 of a round
-//   of 256x256 tiles (measured at 132 to 896 tiles of 256x256), so they pay
-//   where 256x256 tiles leave a last round partly empty and lose where that
-//   round is nearly full.  Measured (256x256 / 256x128 tiles):
-//   2600x2900x1024 22.7 / 17.9 us (132 tiles of 256x256; 1 round against 1),
-//   4352x4096x640 25.4 / 23.0 us (272; 2 rounds against 3), 4096x6144x2048
-//   55.9 / 55.2 us (384; 2 against 3); 3072x4096x1024 18.5 / 21.4 us (192;
-//   1 against 2), 4096x8192x2048 66.4 / 76.0 us (512; 2 against 4),
-//   4096x14336x4096 197.9 / 225.0 us (896; 4 against 7).
+//   256x128 tiles in place of 256x256 ones when they need at most 1.5 times
+//   the rounds: a round of 256x128 tiles costs 0.57-0.66 of a round of
+//   256x256 tiles in mode (b) and 0.5-0.65 in mode (a) (measured at 132 to
+//   896 tiles of 256x256), so they pay where 256x256 tiles leave a last round
+//   partly empty and lose where that round is nearly full.  Measured, mode (b)
+//   (256x256 / 256x128 tiles): 2600x2900x1024 22.7 / 17.9 us (132 tiles of
+//   256x256; 1 round against 1), 4352x4096x640 25.4 / 23.0 us (272; 2 rounds
+//   against 3), 4096x6144x2048 55.9 / 55.2 us (384; 2 against 3);
+//   3072x4096x1024 18.5 / 21.4 us (192; 1 against 2), 4096x8192x2048 66.4 /
+//   76.0 us (512; 2 against 4), 4096x14336x4096 197.9 / 225.0 us (896; 4
+//   against 7).  Mode (a): 2600x2900 at K = 1024 / 4096 / 8192 22.1 / 17.6,
+//   45.4 / 35.7, 72.9 / 58.4 us (1 round against 1); 4608x4608x1024 31.5 /
+//   29.2 us, 4608x4608x8192 153.0 / 151.2 us, 4096x6144x1024 31.9 / 29.6 us,
+//   4864x4096x4096 83.1 / 80.4 us (2 against 3); 3072x4096x1024 18.0 /
+//   18.1 us (1 against 2: not taken).  The mode (a) spill shapes above keep
+//   128x128 tiles: 4352x4096 at K = 1024 ran 29.3 us on them against 30.9 us
+//   on 256x128 tiles.
 //   Only 128x128 tiles split: the 256x256 split kernel would spill around its
 //   last step.
 struct Schedule {
@@ -1288,11 +1305,9 @@ static Schedule gemm_schedule(int64_t m, int64_t n, int64_t k, bool mx, int cus)
         }
         return {128, {(int)tiles128, 1}};
     }
-    if (mx) {
-        const int64_t tiles_h = ((m + 255) / 256) * ((n + 127) / 128);   // 256x128 tiles
-        const int64_t rounds = (tiles256 + cus - 1) / cus, rounds_h = (tiles_h + cus - 1) / cus;
-        if (2 * rounds_h <= 3 * rounds) return {TILE_256x128, {(int)tiles_h, 1}};
-    }
+    const int64_t tiles_h = ((m + 255) / 256) * ((n + 127) / 128);   // 256x128 tiles
+    const int64_t rounds = (tiles256 + cus - 1) / cus, rounds_h = (tiles_h + cus - 1) / cus;
+    if (2 * rounds_h <= 3 * rounds) return {TILE_256x128, {(int)tiles_h, 1}};
     return {256, {(int)tiles256, 1}};
 }
 
@@ -1345,11 +1360,10 @@ hipError_t launch_fmt(int64_t m, int64_t n, int64_t k, const uint8_t* A, const u
         if (sc.tile == TILE_64x128)
             return launch_tiled<MX, FA, FB, TILE_64x128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp,
                                                          fixed_ws, stream);
-    } else {
-        if (sc.tile == TILE_256x128)
-            return launch_tiled<MX, FA, FB, TILE_256x128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp,
-                                                          fixed_ws, stream);
     }
+    if (sc.tile == TILE_256x128)
+        return launch_tiled<MX, FA, FB, TILE_256x128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp,
+                                                      fixed_ws, stream);
     if (sc.tile == 128)
         return launch_tiled<MX, FA, FB, 128>(m, n, k, A, B, sa, sb, ea, eb, D, out_f32, dev, cus, sc.sp, fixed_ws,
                                              stream);

@@ -391,8 +391,8 @@ int fp8g_roof_stream(const void* src, int64_t bytes, void* dst, int write_ratio,
  *                  (mode 0 also when they spill just past one round); in mode
  *                  0, 64 x 128 when 128 x 128 tiles would still leave half of
  *                  the CUs idle and splitting them over K is not predicted
- *                  faster; in mode 1, 256 x 128 in place of 256 x 256 when
- *                  they need at most 1.5 times the rounds of workgroups.
+ *                  faster; 256 x 128 in place of 256 x 256 when they need at
+ *                  most 1.5 times the rounds of workgroups (both modes).
  * split            1, or the number of K ranges (2..4) each of the last
  *                  round's 128 x 128 tiles is split into (mode 0, k a multiple
  *                  of 128; such launches use the split workspace described at

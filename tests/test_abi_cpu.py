@@ -305,6 +305,11 @@ SCHEDULES_256 = [
     ((2561, 3000, 1056, 1), (256, 256, 1, 0)),      # 264 of 256x128: twice the rounds
     ((3072, 4096, 1024, 1), (256, 256, 1, 0)),      # 192 of 256x256 (1 round) against 384 (2)
     ((4096, 8192, 2048, 1), (256, 256, 1, 0)),      # 2 rounds against 4
+    ((2600, 2900, 1024, 0), (256, 128, 1, 0)),      # mode (a) the same
+    ((4864, 4096, 4096, 0), (256, 128, 1, 0)),      # 304 of 256x256 (2 rounds), 608 of 256x128 (3)
+    ((4000, 6400, 256, 0), (256, 256, 1, 0)),       # 400 (2 rounds) against 800 (4)
+    ((3072, 4096, 1024, 0), (256, 256, 1, 0)),
+    ((4352, 4096, 1024, 0), (128, 128, 1, 0)),      # the spill rule comes first
     ((1000, 1001, 272, 0), (64, 128, 1, 0)),        # K tail
     ((300, 512, 0, 0), (64, 128, 1, 0)),            # k = 0
 ]

@@ -60,18 +60,24 @@ def uscale(seed, n, stream=3):
 # 256-CU part: problems whose 128x128 tiles would fill at most half of the CUs
 # (and are not split over K) run on 64x128 tiles, every shape here up to
 # 1000 x 1024; 1900 x 2000 (240 tiles of 128) and 2048 x 2048 (256) run on
-# 128x128 tiles; 2561 x 3000 (11 x 12 tiles of 256) and larger take the
-# 256x256 kernels, with ragged m, n and a K tail.  The epilogue depends on N:
-# bf16 is staged through LDS for N % 8 == 0, fp32 for N % 32 == 0 (1000 x
-# 1024, 2048 x 2048, 2600 x 3072, 2561 x 3008); other N store from registers.
-# 4864 x 4096 and 4864 x 4032 have 304 tiles of 256 for 256 workgroups: a
-# workgroup runs a second tile, so its epilogue borrows a ring slot while the
-# next tile's loads are in flight.  4352 x 4096 (272 tiles of 256, just past
-# one round) runs on 1088 tiles of 128.
+# 128x128 tiles; 2561 x 3000 (11 x 12 tiles of 256), 2600 x 3072 and larger
+# take the 256x256 kernels, with ragged m, n and a K tail.  The epilogue
+# depends on N: bf16 is staged through LDS for N % 8 == 0, fp32 for N % 32 ==
+# 0 (1000 x 1024, 2048 x 2048, 2600 x 3072, 2561 x 3008, 4000 x 6400); other
+# N store from registers.  4000 x 6400 and 4000 x 6201 have 400 tiles of 256
+# for 256 workgroups: a workgroup runs a second tile, so its epilogue borrows
+# a ring slot while the next tile's loads are in flight.  256x128 tiles,
+# where the 256x256 tiles leave a last round partly empty: 2600 x 2900 and
+# 2600 x 2904 (253 tiles, one round; the epilogue from registers, or bf16
+# staged, with and without a K tail), 4864 x 4096 and 4864 x 4032 (608
+# tiles, three rounds; staged, with a K tail); their tile's sa, sb sit beside
+# the ring, not in the borrowed slot.  4352 x 4096 (272 tiles of 256, just
+# past one round) runs on 1088 tiles of 128.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
             (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (1900, 2000, 1024),
-            (2048, 2048, 256), (2561, 3000, 272), (2561, 3008, 272), (2600, 2900, 1024), (2600, 3072, 1024),
-            (4864, 4096, 256), (4864, 4032, 272), (4352, 4096, 272)]
+            (2048, 2048, 256), (2561, 3000, 272), (2561, 3008, 272), (2600, 2900, 1024), (2600, 2904, 1056),
+            (2600, 3072, 1024), (4864, 4096, 256), (4864, 4032, 272), (4000, 6400, 256), (4000, 6201, 272),
+            (4352, 4096, 272)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -379,11 +385,10 @@ def test_mode_b_scale_association_256_tiles(gpu_lib, M, N, K):
 # Neutral block scales (code 127) make mode (b) compute mode (a) with unit
 # scales through the same matrix-core instruction, so the two must agree bit
 # for bit, whatever tiles each takes: each output sums its K steps in the same
-# order.  On 4864 x 4096 (304 tiles of 256x256 in mode (a), 608 of 256x128 in
-# mode (b)) and 4096 x 8192 (512 tiles of 256x256 in both) workgroups run
-# second tiles, and the fp32 outputs come from different epilogues -- staged
-# through LDS in mode (a), from registers in mode (b) -- which this compares
-# exactly.
+# order.  On 4864 x 4096 (608 tiles of 256x128 in both modes) and 4096 x 8192
+# (512 tiles of 256x256 in both) workgroups run second tiles, and the fp32
+# outputs come from different epilogues -- staged through LDS in mode (a),
+# from registers in mode (b) -- which this compares exactly.
 @pytest.mark.parametrize("M,N,K,out", [(300, 260, 1024, "f32"), (4864, 4096, 1024, "f32"),
                                        (4864, 4096, 1024, "bf16"), (4096, 8192, 1024, "f32")])
 def test_mode_b_neutral_scales_equal_mode_a(gpu_lib, M, N, K, out):

@@ -64,10 +64,11 @@ def check_scaled(fp8g, A, fa, B, fb, sa, sb, out, what):
 
 
 # on a 256-CU part the shapes up to 1000 x 1001 run on 64x128 tiles, 1900 x
-# 2000 (240 tiles of 128) on 128x128 tiles, and 2561 x 3000 (more than half as
-# many 256x256 tiles as CUs) on 256x256 tiles
+# 2000 (240 tiles of 128) on 128x128 tiles, 2561 x 3000 (more than half as
+# many 256x256 tiles as CUs) on 256x256 tiles and 2600 x 2904 (132 tiles of
+# 256x256, 253 of 256x128) on 256x128 tiles
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (1, 513, 2048),
-            (1000, 1001, 272), (1900, 2000, 1024), (2561, 3000, 272)]
+            (1000, 1001, 272), (1900, 2000, 1024), (2561, 3000, 272), (2600, 2904, 1056)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])

@@ -72,10 +72,11 @@ def test_graph_replays_match_eager(gpu_lib):
 
 def test_gemm_deterministic_both_tile_sizes(gpu_lib):
     """Repeated launches give identical bits, on 256x256 tiles (2561 x 3000,
-    above the small-problem threshold) and on small-problem tiles (700 x 900:
-    64x128 in mode (a), 128x128 in mode (b)), in both modes."""
+    above the small-problem threshold), on 256x128 tiles (2600 x 2900) and on
+    small-problem tiles (700 x 900: 64x128 in mode (a), 128x128 in mode (b)),
+    in both modes."""
     import torch
-    for (M, N, K) in ((2561, 3000, 1024), (700, 900, 1024)):
+    for (M, N, K) in ((2561, 3000, 1024), (2600, 2900, 1024), (700, 900, 1024)):
         A = torch.from_numpy(synth.u8_codes(51, 1, (M, K))).cuda()
         B = torch.from_numpy(synth.u8_codes(51, 2, (N, K))).cuda()
         sa = torch.rand(M, device="cuda") + 0.5
