@@ -70,14 +70,16 @@ def uscale(seed, n, stream=3):
 # where the 256x256 tiles leave a last round partly empty: 2600 x 2900 and
 # 2600 x 2904 (253 tiles, one round; the epilogue from registers, or bf16
 # staged, with and without a K tail), 4864 x 4096 and 4864 x 4032 (608
-# tiles, three rounds; staged, with a K tail); their tile's sa, sb sit beside
-# the ring, not in the borrowed slot.  4352 x 4096 (272 tiles of 256, just
+# tiles, three rounds; staged, with a K tail, and with one stage per tile, so
+# that a workgroup's next tile reloads the tile scales right after an
+# epilogue); their tile's sa, sb sit beside the ring, not in the borrowed
+# slot.  4352 x 4096 (272 tiles of 256, just
 # past one round) runs on 1088 tiles of 128.
 SHAPES_A = [(1, 1, 16), (33, 65, 48), (256, 256, 128), (300, 200, 512), (257, 1000, 4112), (512, 768, 1024),
             (1, 513, 2048), (640, 3, 160), (1000, 1001, 272), (1000, 1024, 272), (1900, 2000, 1024),
             (2048, 2048, 256), (2561, 3000, 272), (2561, 3008, 272), (2600, 2900, 1024), (2600, 2904, 1056),
-            (2600, 3072, 1024), (4864, 4096, 256), (4864, 4032, 272), (4000, 6400, 256), (4000, 6201, 272),
-            (4352, 4096, 272)]
+            (2600, 3072, 1024), (4864, 4096, 256), (4864, 4032, 272), (4864, 4096, 128), (4864, 4032, 48),
+            (4000, 6400, 256), (4000, 6201, 272), (4352, 4096, 272)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
@@ -306,10 +308,12 @@ def mx_scales(seed, R, nb, stream):
 # tiles of 256x256, 253 of 256x128: one round either way) the 256x128 tiles;
 # 2561 x 3000 (264 of 256x128: two rounds) and 2304 x 4000 (144 tiles of
 # 256x256, 288 of 256x128) the 256x256 tiles.  Ragged m and n throughout,
-# with and without a K tail.
+# with and without a K tail.  4864 x 4096 x 128 and 4864 x 4032 x 96: 608
+# tiles of 256x128 (three per workgroup at most) of one stage each, with
+# whole scale dwords (one partial group per tile) and byte-wise scales.
 SHAPES_B = [(32, 32, 32), (64, 96, 96), (256, 256, 256), (257, 300, 4128), (512, 512, 1024), (5, 700, 160),
             (300, 7, 64), (2561, 3000, 1056), (2600, 2900, 1024), (2600, 2900, 1056), (2304, 4000, 1024),
-            (2304, 4000, 1056)]
+            (2304, 4000, 1056), (4864, 4096, 128), (4864, 4032, 96)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])
