@@ -14,12 +14,19 @@
 //     (the nearest of the format's decoded magnitudes, ties to the even code)
 //     and as integer bit manipulation of the fp32 input.
 //   * The row-wise quantizer: s = fp32(amax / MAX), q = cast(fp32(x / s)).
+//   * The MX block quantizer (page "[sglang] FlashInfer v0.6.7 MXFP8 Gemm
+//     통합", section 1): per 32 elements of a row the smallest power of two
+//     2^e with amax <= 448 * 2^e, q = cast(x * 2^-e), scale code e + 127.
 //   * Mode (a): D = sa[m] sb[n] sum_k dec(A[m,k]) dec(B[n,k]) in double, and
-//     mode (b): D = sum_j 2^(ea+eb-254) sum_{t<32} dec dec (page "[sglang]
-//     FlashInfer v0.6.7 MXFP8 Gemm 통합", sections 1-2), plain loops.
+//     mode (b): D = sum_j 2^(ea+eb-254) sum_{t<32} dec dec (the MXFP8 page,
+//     sections 1-2), plain loops, each with the weight of the error bound
+//     (the same sums over |products|).
 //   * The matrix-core truncation term T of the error bound (the same
-//     definition as oracle.gemm.alignment_term), threaded over output columns,
-//     for checks of full-size results.
+//     definition as oracle.gemm.alignment_term).
+//
+// The quantizers, GEMMs and T split their rows or output columns over host
+// threads, for checks of full-size results; every output is still one
+// sequential loop, so the thread count does not change any result.
 //
 // Build: g++ -O2 -shared -fPIC -pthread (no vector intrinsics).  C entry points only.
 
@@ -42,6 +49,20 @@ constexpr Fmt E4M3{4, 3, 7, false, 0x7E};
 constexpr Fmt E5M2{5, 2, 15, true, 0x7B};
 
 const Fmt& fmt_of(int f) { return f == 1 ? E5M2 : E4M3; }
+
+// fn(lo, hi) over [0, n) in `threads` contiguous ranges (<= 0: all hardware threads).
+template <class Fn>
+void parallel_ranges(int64_t n, int threads, Fn fn) {
+    int nt = threads > 0 ? threads : (int)std::max(1u, std::thread::hardware_concurrency());
+    nt = (int)std::min<int64_t>(nt, std::max<int64_t>(n, 1));
+    if (nt <= 1) {
+        fn((int64_t)0, n);
+        return;
+    }
+    std::vector<std::thread> pool;
+    for (int i = 0; i < nt; ++i) pool.emplace_back(fn, n * i / nt, n * (i + 1) / nt);
+    for (auto& th : pool) th.join();
+}
 
 double decode(const Fmt& F, uint8_t c) {
     const int s = c >> 7;
@@ -174,52 +195,106 @@ void fp8o_encode_array(int fmt, const float* x, int64_t n, uint8_t* q) {
 }
 
 // Row-wise quantizer: s[r] = fp32(max_c |x| / MAX); q = cast(fp32(x / s)); s == 0 gives signed zeros.
-void fp8o_quantize_rowwise(int fmt, const float* x, int64_t rows, int64_t cols, uint8_t* q, float* s) {
+void fp8o_quantize_rowwise(int fmt, const float* x, int64_t rows, int64_t cols, uint8_t* q, float* s, int threads) {
     const Fmt& F = fmt_of(fmt);
     const float maxv = (float)mags_of(F).v[F.max_code];
-    for (int64_t r = 0; r < rows; ++r) {
-        float amax = 0.0f;
-        for (int64_t c = 0; c < cols; ++c) amax = std::fmax(amax, std::fabs(x[r * cols + c]));
-        const float sr = amax / maxv;
-        s[r] = sr;
-        for (int64_t c = 0; c < cols; ++c) {
-            const float v = x[r * cols + c];
-            const float y = sr == 0.0f ? std::copysign(0.0f, v) : v / sr;
-            q[r * cols + c] = encode_nearest(F, y);
-        }
-    }
-}
-
-// Mode (a) in double: D[m,n] = sa[m] sb[n] sum_k dec(A[m,k]) dec(B[n,k]).
-void fp8o_gemm_scaled(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
-                      const float* sa, const float* sb, double* D) {
-    const Fmt& FA = fmt_of(fmt_a);
-    const Fmt& FB = fmt_of(fmt_b);
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n) {
-            double acc = 0.0;
-            for (int64_t k = 0; k < K; ++k) acc += decode(FA, A[m * K + k]) * decode(FB, B[n * K + k]);
-            D[m * N + n] = acc * (double)sa[m] * (double)sb[n];
-        }
-}
-
-// Mode (b) in double: D[m,n] = sum_j 2^(ea[m,j]-127) 2^(eb[n,j]-127) sum_{t<32} dec(A) dec(B).
-void fp8o_gemm_mx(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
-                  const uint8_t* ea, const uint8_t* eb, double* D) {
-    const Fmt& FA = fmt_of(fmt_a);
-    const Fmt& FB = fmt_of(fmt_b);
-    const int64_t nb = K / 32;
-    for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n) {
-            double acc = 0.0;
-            for (int64_t j = 0; j < nb; ++j) {
-                double blk = 0.0;
-                for (int64_t t = 0; t < 32; ++t)
-                    blk += decode(FA, A[m * K + 32 * j + t]) * decode(FB, B[n * K + 32 * j + t]);
-                acc += std::ldexp(blk, (int)ea[m * nb + j] + (int)eb[n * nb + j] - 254);
+    parallel_ranges(rows, threads, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r) {
+            float amax = 0.0f;
+            for (int64_t c = 0; c < cols; ++c) amax = std::fmax(amax, std::fabs(x[r * cols + c]));
+            const float sr = amax / maxv;
+            s[r] = sr;
+            for (int64_t c = 0; c < cols; ++c) {
+                const float v = x[r * cols + c];
+                const float y = sr == 0.0f ? std::copysign(0.0f, v) : v / sr;
+                q[r * cols + c] = encode_nearest(F, y);
             }
-            D[m * N + n] = acc;
         }
+    });
+}
+
+// MX block quantizer, E4M3 elements and UE8M0 scales, blocks of 32 along a
+// row (cols % 32 == 0, finite inputs): e = the smallest integer with
+// amax <= 448 * 2^e, at least -127 (an all-zero block takes -127);
+// q = cast(x * 2^-e), exact in double and in fp32 wherever the cast can give a
+// nonzero code; the scale code is e + 127.
+void fp8o_mx_quantize(const float* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e, int threads) {
+    const int64_t nb = cols / 32;
+    const double maxv = mags_of(E4M3).v[E4M3.max_code];
+    parallel_ranges(rows, threads, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t j = 0; j < nb; ++j) {
+                const float* xb = x + r * cols + 32 * j;
+                double amax = 0.0;
+                for (int t = 0; t < 32; ++t) amax = std::max(amax, std::fabs((double)xb[t]));
+                int ex = -127;
+                if (amax > 0.0) {
+                    int fe;
+                    std::frexp(amax, &fe);   // 2^(fe-1) <= amax < 2^fe, so 448 * 2^(fe-10) < amax
+                    ex = fe - 10;
+                    while (amax > std::ldexp(maxv, ex)) ++ex;
+                    ex = std::max(ex, -127);
+                }
+                e[r * nb + j] = (uint8_t)(ex + 127);
+                for (int t = 0; t < 32; ++t)
+                    q[r * cols + 32 * j + t] = encode_nearest(E4M3, (float)std::ldexp((double)xb[t], -ex));
+            }
+    });
+}
+
+// Mode (a) in double: D[m,n] = sa[m] sb[n] sum_k dec(A[m,k]) dec(B[n,k]), and
+// (W not null) the bound's weight W[m,n] = |sa[m] sb[n]| sum_k |dec(A[m,k]) dec(B[n,k])|.
+void fp8o_gemm_scaled(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
+                      const float* sa, const float* sb, double* D, double* W, int threads) {
+    double da[256], db[256];
+    for (int c = 0; c < 256; ++c) {
+        da[c] = decode(fmt_of(fmt_a), (uint8_t)c);
+        db[c] = decode(fmt_of(fmt_b), (uint8_t)c);
+    }
+    parallel_ranges(N, threads, [&](int64_t n0, int64_t n1) {
+        for (int64_t n = n0; n < n1; ++n)
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < K; ++k) {
+                    const double p = da[A[m * K + k]] * db[B[n * K + k]];
+                    acc += p;
+                    mag += std::fabs(p);
+                }
+                D[m * N + n] = acc * (double)sa[m] * (double)sb[n];
+                if (W) W[m * N + n] = mag * std::fabs((double)sa[m]) * std::fabs((double)sb[n]);
+            }
+    });
+}
+
+// Mode (b) in double: D[m,n] = sum_j 2^(ea[m,j]-127) 2^(eb[n,j]-127) sum_{t<32} dec(A) dec(B),
+// and (W not null) W[m,n], the same sum over |products|.
+void fp8o_gemm_mx(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t* A, const uint8_t* B,
+                  const uint8_t* ea, const uint8_t* eb, double* D, double* W, int threads) {
+    double da[256], db[256];
+    for (int c = 0; c < 256; ++c) {
+        da[c] = decode(fmt_of(fmt_a), (uint8_t)c);
+        db[c] = decode(fmt_of(fmt_b), (uint8_t)c);
+    }
+    const int64_t nb = K / 32;
+    parallel_ranges(N, threads, [&](int64_t n0, int64_t n1) {
+        for (int64_t n = n0; n < n1; ++n)
+            for (int64_t m = 0; m < M; ++m) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t j = 0; j < nb; ++j) {
+                    double blk = 0.0, bmag = 0.0;
+                    for (int64_t t = 0; t < 32; ++t) {
+                        const double p = da[A[m * K + 32 * j + t]] * db[B[n * K + 32 * j + t]];
+                        blk += p;
+                        bmag += std::fabs(p);
+                    }
+                    const int x = (int)ea[m * nb + j] + (int)eb[n * nb + j] - 254;
+                    acc += std::ldexp(blk, x);
+                    mag += std::ldexp(bmag, x);
+                }
+                D[m * N + n] = acc;
+                if (W) W[m * N + n] = mag;
+            }
+    });
 }
 
 // Matrix-core truncation term, unscaled: T[m,n] = sum over runs g of 8
@@ -283,11 +358,7 @@ void fp8o_alignment_term(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, 
             }
         }
     };
-    int nt = threads > 0 ? threads : (int)std::max(1u, std::thread::hardware_concurrency());
-    nt = (int)std::min<int64_t>(nt, std::max<int64_t>(N, 1));
-    std::vector<std::thread> pool;
-    for (int i = 0; i < nt; ++i) pool.emplace_back(work, N * i / nt, N * (i + 1) / nt);
-    for (auto& th : pool) th.join();
+    parallel_ranges(N, threads, work);
 }
 
 }  // extern "C"

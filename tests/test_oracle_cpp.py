@@ -120,3 +120,55 @@ def test_cpp_alignment_term_matches_numpy(fmt_a, fmt_b):
     ref = gemm.alignment_term(A, B, ea=ea, eb=eb, fmt_a=fmt_a, fmt_b=fmt_b)
     got = cpp_oracle.alignment_term(A, B, ea=ea, eb=eb, fmt_a=fmt_a, fmt_b=fmt_b)
     np.testing.assert_allclose(got, ref, rtol=1e-13, atol=0)
+
+
+def test_mx_quantize_agrees():
+    """The C++ MX block quantizer against the numpy oracle's (two independent
+    restatements of the MXFP8 page's rule), bit for bit, on the MX workload's
+    recipe and on edge blocks; plus one block worked by hand: 32 ones have
+    amax 1, the smallest e with 1 <= 448 * 2^e is -8 (448/256 = 1.75, 448/512
+    = 0.875), so the scale code is 127 - 8 = 119 and every element is
+    1 * 2^8 = 256 = 2^8, E4M3 exponent field 8 + 7 = 15, mantissa 0: 0x78."""
+    w = synth.WORKLOADS["c5_mx_4096x14336x4096"]
+    x = synth.draw(w, "a", slice(0, 24))[:, :1024].copy()
+    x[0, :32] = 1.0                                   # the hand-worked block
+    x[1, :32] = 0.0                                   # all zero: e = -127
+    x[1, 32:64] = 448.0                               # amax exactly 448: e = 0
+    x[1, 64:96] = np.float32(448.0 * 8)               # exactly 448 * 2^3: e = 3
+    x[1, 96] = np.nextafter(np.float32(448.0), np.float32(1e9))   # just above 448: e = 1
+    x[1, 128:160] = np.float32(2.0 ** -149)           # fp32 subnormal: e = -127, codes 0
+    x[1, 160:192] *= np.float32(1e-30)
+    x[1, 192:224] *= np.float32(1e30)
+    q1, e1 = cpp_oracle.mx_quantize(x, threads=3)
+    q2, e2 = quant.mx_quantize(x)
+    assert np.array_equal(e1, e2) and np.array_equal(q1, q2)
+    assert (q1[0, :32] == 0x78).all() and e1[0, 0] == 119
+    assert e1[1, 0] == 0 and e1[1, 1] == 127 and e1[1, 2] == 130 and e1[1, 3] == 128 and e1[1, 4] == 0
+    assert (q1[1, 128:160] == 0).all()
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+def test_gemm_weight_and_threads(fa, fb):
+    """The C++ GEMMs' bound weight W equals the numpy oracle's (exactly for
+    E4M3 x E4M3, whose |product| sums are exact in double), and the results
+    do not depend on the number of threads."""
+    M, N, K = 6, 11, 224
+    A, B = _codes(41, (M, K), fa), _codes(42, (N, K), fb)
+    sa = (0.5 + synth.uniform(synth.stream_key(43, 1), 0, M)).astype(np.float32)
+    sb = (0.5 + synth.uniform(synth.stream_key(43, 2), 0, N)).astype(np.float32)
+    D1, W1 = cpp_oracle.gemm_scaled(A, B, sa, sb, fa, fb, weight=True, threads=1)
+    D5, W5 = cpp_oracle.gemm_scaled(A, B, sa, sb, fa, fb, weight=True, threads=5)
+    assert np.array_equal(D1, D5) and np.array_equal(W1, W5)
+    Wn = gemm.gemm_scaled_weight(A, B, sa, sb, fa, fb)
+    if fa == fb == "e4m3":
+        assert np.array_equal(W1, Wn)
+    np.testing.assert_allclose(W1, Wn, rtol=1e-13, atol=0)
+    ea = (synth.u8_codes(44, 3, (M, K // 32)) % 41 + 107).astype(np.uint8)
+    eb = (synth.u8_codes(45, 4, (N, K // 32)) % 41 + 107).astype(np.uint8)
+    X1, XW1 = cpp_oracle.mxfp8_gemm(A, B, ea, eb, fa, fb, weight=True, threads=1)
+    X4, XW4 = cpp_oracle.mxfp8_gemm(A, B, ea, eb, fa, fb, weight=True, threads=4)
+    assert np.array_equal(X1, X4) and np.array_equal(XW1, XW4)
+    np.testing.assert_allclose(XW1, gemm.mxfp8_gemm_weight(A, B, ea, eb, fa, fb), rtol=1e-13, atol=0)
+    q1, s1 = cpp_oracle.quantize_rowwise(synth.draw(synth.WORKLOADS["c3_8192x2048x8192"], "a", slice(0, 9)), threads=1)
+    q4, s4 = cpp_oracle.quantize_rowwise(synth.draw(synth.WORKLOADS["c3_8192x2048x8192"], "a", slice(0, 9)), threads=4)
+    assert np.array_equal(q1, q4) and np.array_equal(s1.view(np.uint32), s4.view(np.uint32))
