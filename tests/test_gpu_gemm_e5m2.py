@@ -145,10 +145,10 @@ def test_ex_dtype_checks(gpu_lib):
 
 
 # K / 128 = 3 and 5: the last group of 4 stages' block scales is partial.  On
-# a 256-CU part 2600 x 2900 runs on 256x128 tiles and 2304 x 4000 (K tail) on
-# 256x256 tiles; the rest on 128x128 tiles.
+# a 256-CU part 2600 x 2900 runs on 256x128 tiles (with and without a K tail)
+# and 2304 x 4000 (K tail) on 256x256 tiles; the rest on 128x128 tiles.
 SHAPES_B = [(32, 32, 32), (64, 96, 96), (257, 300, 4128), (512, 512, 1024), (5, 700, 160), (2600, 2900, 1024),
-            (2304, 4000, 160), (300, 260, 384), (200, 300, 640)]
+            (2600, 2900, 1056), (2304, 4000, 160), (300, 260, 384), (200, 300, 640)]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f32"])

@@ -30,13 +30,14 @@ def _call(lib, name, M, N, K, A, B, sa, sb, D, out):
 
 
 # 512x512x8192: 16 tiles of 128, each split into 4 K ranges; 128x128x4096: one
-# tile in 4; 1000x1001x272: no split (K tail; 64x128 tiles)
+# tile in 4; 1000x1001x272: no split (K tail; 64x128 tiles); 2600x2900x1024:
+# 253 tiles of 256x128
 @pytest.mark.parametrize("out", [0, 1])
 def test_noalloc_matches_fp8_gemm_scaled(gpu_lib, out):
     import torch
     lib = gpu_lib.load()
     dt = torch.bfloat16 if out == 0 else torch.float32
-    for M, N, K in ((512, 512, 8192), (128, 128, 4096), (1000, 1001, 272)):
+    for M, N, K in ((512, 512, 8192), (128, 128, 4096), (1000, 1001, 272), (2600, 2900, 1024)):
         seed = 7 * M + N + K
         A, B = to_dev(_codes(seed, (M, K), 1)), to_dev(_codes(seed, (N, K), 2))
         sa = to_dev((0.5 + synth.uniform(synth.stream_key(seed, 3), 0, M)).astype(np.float32))
