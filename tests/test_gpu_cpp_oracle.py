@@ -10,11 +10,11 @@ results:
     T the matrix-core truncation term (the C++ loop of oracle.gemm's
     definition), at ragged shapes on every tile shape (64x128, 128x128, split
     over K, 256x128, 256x256) with every element compared;
-  * the full-size workloads in the benchmark's launch configuration: the
-    GPU's quantized operands against the C++ quantizers' (activations on the
-    sampled rows, weights on every row), and D on one row in every 128-row
-    band against every column, with the plain-bound ceilings of
-    test_gpu_gemm.
+  * the full-size workloads in the benchmark's launch configurations (also
+    the FFN-up step with E5M2 operands): the GPU's quantized operands against
+    the C++ quantizers' (activations on the sampled rows, weights on every
+    row), and D on one row in every 128-row band against every column, with
+    ceilings on the elements over the plain bound (test_gpu_gemm's for E4M3).
 Every input comes from the seeded generators and the C++ quantizers, none from
 the GPU.
 """
@@ -28,6 +28,10 @@ from oracle import cpp_oracle
 from test_gpu_gemm import PLAIN_MAX, band_rows
 
 pytestmark = pytest.mark.gpu
+
+# Elements over the plain bound (T = 0) on the sampled rows of the FFN-up step
+# with E5M2 operands, recorded with margin: 5 (bf16) and 1077 (fp32) of 1453056.
+PLAIN_MAX_E5M2 = {"bf16": 8, "f32": 1200}
 
 
 def _codes(t):
@@ -116,9 +120,11 @@ def test_mode_b_matches_cpp(gpu_lib, M, N, K, out):
                       alignment(A, B, ea=ea, eb=eb))
 
 
-def _full_size(gpu_lib, w, mx):
+def _full_size(gpu_lib, w, mx, fmt="e4m3"):
     """GPU quantize -> GPU GEMM at full size (bf16, the benchmark's launch, and
-    fp32), against the C++ quantizers and the C++ GEMM."""
+    fp32), against the C++ quantizers and the C++ GEMM.  fmt: both operands'
+    format in mode (a) (E5M2: fp8_quantize_ex and fp8_gemm_scaled_ex, as the
+    benchmark's --fmt-a e5m2 --fmt-b e5m2 step)."""
     import torch
     rows = band_rows(w.M)
     say("C++ full size", w.name, "draw")
@@ -128,6 +134,12 @@ def _full_size(gpu_lib, w, mx):
         qa, sa = gpu_lib.mxfp8_quantize(to_dev(XA))
         qb, sb = gpu_lib.mxfp8_quantize(to_dev(XB))
         gemm_fn = gpu_lib.mxfp8_gemm
+    elif fmt == "e5m2":
+        F = gpu_lib.FMT_E5M2
+        qa, sa = gpu_lib.fp8_quantize_ex(to_dev(XA), fmt=F)
+        qb, sb = gpu_lib.fp8_quantize_ex(to_dev(XB), fmt=F)
+        gemm_fn = lambda m, n, k, a, b, x, y, out_dtype: gpu_lib.fp8_gemm_scaled_ex(m, n, k, a, F, b, F, x, y,
+                                                                                    out_dtype=out_dtype)
     else:
         qa, sa = gpu_lib.fp8_quantize_rowwise(to_dev(XA))
         qb, sb = gpu_lib.fp8_quantize_rowwise(to_dev(XB))
@@ -139,7 +151,7 @@ def _full_size(gpu_lib, w, mx):
         Ds[out] = to_host(D[torch.from_numpy(rows).cuda()])
         del D
     say("C++ full size", w.name, "oracle")
-    quantize = cpp_oracle.mx_quantize if mx else cpp_oracle.quantize_rowwise
+    quantize = cpp_oracle.mx_quantize if mx else (lambda x: cpp_oracle.quantize_rowwise(x, fmt))
     oa, osa = quantize(XA[rows])
     ob, osb = quantize(XB)
     del XA, XB
@@ -153,11 +165,11 @@ def _full_size(gpu_lib, w, mx):
     else:
         assert np.array_equal(sa_h[rows].view(np.uint32), osa.view(np.uint32))
         assert np.array_equal(sb_h.view(np.uint32), osb.view(np.uint32))
-        ref, W = cpp_oracle.gemm_scaled(oa, ob, osa, osb, weight=True)
-        T = alignment(oa, ob, osa, osb)
+        ref, W = cpp_oracle.gemm_scaled(oa, ob, osa, osb, fmt, fmt, weight=True)
+        T = alignment(oa, ob, osa, osb, fmt_a=fmt, fmt_b=fmt)
     for out in ("bf16", "f32"):
-        assert_gemm_close(Ds[out], ref, W, out, "%s vs C++ %s" % (w.name, out), T,
-                          plain_max=PLAIN_MAX[(w.name, out)])
+        assert_gemm_close(Ds[out], ref, W, out, "%s %s vs C++ %s" % (w.name, fmt, out), T,
+                          plain_max=PLAIN_MAX[(w.name, out)] if fmt == "e4m3" else PLAIN_MAX_E5M2[out])
 
 
 def test_c3_matches_cpp(gpu_lib):
@@ -166,6 +178,10 @@ def test_c3_matches_cpp(gpu_lib):
 
 def test_ffn_up_matches_cpp(gpu_lib):
     _full_size(gpu_lib, synth.WORKLOADS["c4_ffn_up_8192x22016x8192"], mx=False)
+
+
+def test_ffn_up_e5m2_matches_cpp(gpu_lib):
+    _full_size(gpu_lib, synth.WORKLOADS["c4_ffn_up_8192x22016x8192"], mx=False, fmt="e5m2")
 
 
 def test_mx_workload_matches_cpp(gpu_lib):
