@@ -365,3 +365,44 @@ def test_quantize_e5m2_feeds_e5m2_gemm(gpu_lib):
     assert_gemm_close(D, gemm.gemm_scaled(oa, ob, osa, osb, "e5m2", "e4m3"),
                       gemm.gemm_scaled_weight(oa, ob, osa, osb, "e5m2", "e4m3"), "bf16", "e5m2 quantize -> gemm",
                       alignment(oa, ob, osa, osb, fmt_a="e5m2", fmt_b="e4m3"))
+
+
+# The quantize benchmark's six modes (fp8_quantize_ex on the 8192 x 8192 FFN-up
+# activations: fp32 or bf16 input, one scale per row or per tensor, E4M3 or
+# E5M2 codes), at that full size, against the plain C++ oracle bit for bit.  A
+# per-tensor scale is the row-wise rule applied to the tensor as one row.
+BENCH_MODES = [("f32_row_e4m3", False, False, "e4m3"), ("bf16_row_e4m3", True, False, "e4m3"),
+               ("f32_tensor_e4m3", False, True, "e4m3"), ("bf16_tensor_e4m3", True, True, "e4m3"),
+               ("f32_row_e5m2", False, False, "e5m2"), ("bf16_row_e5m2", True, False, "e5m2")]
+
+
+@pytest.fixture(scope="module")
+def ffn_up_activations():
+    return synth.draw(synth.WORKLOADS["c4_ffn_up_8192x22016x8192"], "a")
+
+
+@pytest.mark.parametrize("name,bf16,per_tensor,fmt", BENCH_MODES, ids=[m[0] for m in BENCH_MODES])
+def test_quantize_bench_modes_full_size(gpu_lib, ffn_up_activations, name, bf16, per_tensor, fmt):
+    import torch
+    from oracle import cpp_oracle
+    x = ffn_up_activations
+    if bf16:
+        bits = _bf16_bits(x)
+        xin, x32 = _dev_bf16(bits), quant.bf16_to_f32(bits)
+    else:
+        xin, x32 = to_dev(x), x
+    say("quantize bench mode", name, x.shape)
+    q, s = gpu_lib.fp8_quantize_ex(xin, per_tensor=per_tensor, fmt=E5M2 if fmt == "e5m2" else 0)
+    torch.cuda.synchronize()
+    qg, sg = q.view(torch.uint8).cpu().numpy(), to_host(s)
+    del q, xin
+    if per_tensor:
+        qr, sr = cpp_oracle.quantize_rowwise(x32.reshape(1, -1), fmt)
+        qr = qr.reshape(x.shape)
+    else:
+        qr, sr = cpp_oracle.quantize_rowwise(x32, fmt)
+    assert np.array_equal(sg.view(np.uint32), sr.view(np.uint32)), name + ": scales differ"
+    if not np.array_equal(qg, qr):
+        r, c = np.argwhere(qg != qr)[0]
+        raise AssertionError("%s: %d codes differ; first at (%d,%d): x=%r gpu=%02x oracle=%02x"
+                             % (name, int((qg != qr).sum()), r, c, x32[r, c], qg[r, c], qr[r, c]))
