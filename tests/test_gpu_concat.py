@@ -55,3 +55,19 @@ def test_concat_mla_k_nan_payloads_copied(gpu_lib):
     rope = np.full((2, 1, 64), 0x7C, np.uint8)              # E5M2 infinity pattern
     k = gpu_lib.concat_mla_k(torch.from_numpy(nope).cuda(), torch.from_numpy(rope).cuda())
     assert np.array_equal(k.cpu().numpy(), concat.concat_mla_k(nope, rope))
+
+
+def test_concat_mla_k_benchmark_size(gpu_lib):
+    """The concat_mla benchmark's configuration: FP8 elements, 16384 tokens x
+    128 heads, one rope row shared by a token's heads; every byte of k
+    compared."""
+    import torch
+    T, H = 16384, 128
+    nope = raw(91, (T, H, 128), np.uint8)
+    rope = raw(92, (T, 1, 64), np.uint8)
+    say("concat_mla_k benchmark size", T, H)
+    k = gpu_lib.concat_mla_k(torch.from_numpy(nope).cuda().view(torch.float8_e4m3fn),
+                             torch.from_numpy(rope).cuda().view(torch.float8_e4m3fn))
+    got = k.view(torch.uint8).cpu().numpy()
+    del k
+    assert np.array_equal(got, concat.concat_mla_k(nope, rope))
