@@ -284,6 +284,8 @@ int mxfp8_quantize(const float* x, int64_t rows, int64_t cols,
  * k % 32 != 0 -> ERR_SHAPE.  m == 0 or n == 0: no-op.  k == 0: D = 0.
  * Limits as fp8_gemm_scaled: k >= 2^23, m >= 2^31, n >= 2^22 (bf16) / 2^21
  * (fp32) -> ERR_UNSUPPORTED.
+ * Performance: k % 128 != 0 takes a slower path (scale bytes read one by one
+ * from global memory), about half the rate of k % 128 == 0.
  * Scale code 255 (NaN) and E4M3 NaN codes are outside the contract.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_OVERLAP,
  * ERR_UNSUPPORTED, ERR_HIP.
